@@ -1,0 +1,28 @@
+"""Compile the oracle's C routine (test infrastructure; gcc + OpenMP, no HIP).
+
+    python -m oracle.build      # writes oracle/liboracle_gemm.so
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gemm_int64.c")
+LIB = os.path.join(HERE, "liboracle_gemm.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile gemm_int64.c into liboracle_gemm.so and return its path."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True))
+    sys.exit(0)

@@ -1,0 +1,207 @@
+"""Pins for oracle.gemm, oracle.fold, oracle.kv and oracle.stats (CPU only).
+
+GEMM: the C int64 routine against a second route (float64 BLAS, exact below
+2^53), against Python loops on tiny inputs and a hand-worked example; the
+dequant epilogue against exact rational rounding.  Fold: the full-precision
+invariance X R . R^T W = X W (page "SpinQuant, Reproduced", Q1/Q5), the
+Hadamard fold against a textbook butterfly down the columns, and block
+structure.  KV: Q K^T invariance per head under the head-wise rotation (Q5).
+Kurtosis: closed forms, then the page's claim (Q3) on synthetic outliers.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from rotation_bit_quantization_amd import synth
+from tests import exact
+from tests.test_oracle_hadamard import _textbook_fwht
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ GEMM
+
+def test_gemm_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_examples.json")))["gemm_small"]
+    acc = oracle.gemm_int_codes(np.array(ex["qx"], np.int8), np.array(ex["qw"], np.int8))
+    assert acc.tolist() == ex["acc"]
+
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(1)
+    qx = rng.integers(-7, 8, size=(5, 24)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(3, 24)).astype(np.int8)
+    acc = oracle.gemm_int_codes(qx, qw)
+    for m in range(5):
+        for n in range(3):
+            assert acc[m, n] == sum(int(qx[m, k]) * int(qw[n, k]) for k in range(24))
+
+
+@pytest.mark.parametrize("shape", [(64, 256, 256), (17, 33, 4096), (8, 16, 12288)])
+def test_gemm_c_route_equals_blas_route(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    qx[0] = 7
+    qw[0] = -7                                           # extreme accumulator -49 K
+    a = oracle.gemm_int_codes(qx, qw)
+    assert np.array_equal(a, oracle.gemm_int_codes_blas(qx, qw))
+    assert a[0, 0] == -49 * K
+    rows = np.array([M - 1, 0, M // 2])
+    assert np.array_equal(oracle.gemm_rows(qx, qw, rows), a[rows])
+
+
+def test_dequant_exact_route():
+    rng = np.random.default_rng(2)
+    acc = rng.integers(-600000, 600000, size=(6, 5))
+    sx = (rng.random(6) * 0.3).astype(np.float32)
+    sw = (rng.random(5) * 0.01).astype(np.float32)
+    y = oracle.dequant(acc, sx, sw)
+    for m in range(6):
+        for n in range(5):
+            t = exact.to_f32(Fraction(int(acc[m, n])) * exact.frac(sx[m]))
+            v = exact.to_f32(t * exact.frac(sw[n]))
+            assert Fraction(float(y[m, n])) == v
+    with pytest.raises(OverflowError):
+        oracle.dequant(np.array([[2 ** 31]]), np.ones(1, np.float32), np.ones(1, np.float32))
+
+
+def test_w4a4_from_packed_matches_float_reference():
+    rng = np.random.default_rng(4)
+    qx = rng.integers(-7, 8, size=(8, 64)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(6, 64)).astype(np.int8)
+    sx = rng.random(8).astype(np.float32)
+    sw = rng.random(6).astype(np.float32)
+    y, acc = oracle.w4a4_gemm(oracle.pack_int4(qx), sx, oracle.pack_int4(qw), sw)
+    ref = (qx.astype(np.float64) * sx[:, None].astype(np.float64)) @ \
+          (qw.astype(np.float64) * sw[:, None].astype(np.float64)).T
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ fold
+
+def test_fold_invariance_haar():
+    """Full-precision invariance: (X R)(R^T W) = X W within 1e-4 relative (fp32)."""
+    cfg = synth.tiny_config()
+    x, w, r = cfg["x"], cfg["w"], cfg["r"]
+    assert oracle.orthogonality_error(r) < 1e-5
+    w_rot, _, _ = oracle.fold_rotation(w, r, 256)
+    xr = (x.astype(np.float32) @ r).astype(np.float32)
+    lhs = xr @ w_rot
+    rhs = x.astype(np.float32) @ w
+    rel = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
+    assert rel < 1e-4
+
+
+def test_fold_invariance_r1_4096_subsample():
+    rng = np.random.default_rng(8)
+    r = synth.haar_orthogonal(rng, 1024)
+    w = synth.gaussian_weight(rng, 1024, 48)
+    x = rng.standard_normal((16, 1024)).astype(np.float32)
+    w_rot, _, _ = oracle.fold_rotation(w, r, 1024)
+    rel = np.linalg.norm((x @ r) @ w_rot - x @ w) / np.linalg.norm(x @ w)
+    assert rel < 1e-4
+
+
+@pytest.mark.parametrize("r_block", [16, 64])
+def test_fold_hadamard_equals_textbook_fwht_down_columns(r_block):
+    rng = np.random.default_rng(r_block)
+    K, N = 128, 10
+    w = rng.integers(-100, 100, size=(K, N)).astype(np.float32)
+    w_rot, _, _ = oracle.fold_rotation(w, None, r_block)
+    # H is symmetric for Sylvester orders, so H^T w = FWHT(w) along each column block
+    ref = _textbook_fwht(w.astype(np.int64).T.reshape(N, K // r_block, r_block)).reshape(N, K).T
+    assert np.allclose(w_rot, ref / np.sqrt(r_block), rtol=1e-7, atol=0)
+
+
+def test_fold_h12_uses_transpose():
+    """For the skew H_12 the fold must use H^T: (x H)(H^T w) / 12 = x w exactly."""
+    rng = np.random.default_rng(12)
+    w = rng.integers(-9, 9, size=(12, 3)).astype(np.float32)
+    x = rng.integers(-9, 9, size=(2, 12)).astype(np.float64)
+    w_rot, _, _ = oracle.fold_rotation(w, None, 12)
+    xr = oracle.rotate_rows(x, 12)
+    assert np.allclose(xr @ w_rot.astype(np.float64), x @ w, rtol=1e-6, atol=1e-6)
+    # the untransposed product would not invert the rotation
+    bad = xr @ (oracle.hadamard(12) / np.sqrt(12) @ w)
+    assert not np.allclose(bad, x @ w, atol=1e-3)
+
+
+def test_fold_block_structure_and_weight_layout():
+    rng = np.random.default_rng(3)
+    r = synth.haar_orthogonal(rng, 32)
+    w = synth.gaussian_weight(rng, 96, 20)
+    w_rot, wq, ws = oracle.fold_rotation(w, r, 32)
+    for b in range(3):
+        blk, _, _ = oracle.fold_rotation(w[32 * b:32 * (b + 1)], r, 32)
+        assert np.array_equal(w_rot[32 * b:32 * (b + 1)], blk)
+    assert wq.shape == (20, 48) and ws.shape == (20,)
+    codes = oracle.unpack_int4(wq)
+    for n in (0, 7, 19):
+        s_ex = exact.scale_exact(w_rot[:, n])
+        assert Fraction(float(ws[n])) == s_ex
+        assert codes[n].tolist() == exact.quantize_exact(w_rot[:, n], s_ex)
+
+
+# ------------------------------------------------------------------ KV
+
+def test_kv_qk_invariance_subsample():
+    cfg = synth.kv_config(T=64, H=4)
+    q, k = cfg["q"], cfg["k"]
+    _, _, qr = oracle.kv_quant(q, rotate=True, quantize=False)
+    _, _, kr = oracle.kv_quant(k, rotate=True)
+    for h in range(4):
+        lhs = qr[:, h].astype(np.float32) @ kr[:, h].astype(np.float32).T
+        rhs = q[:, h].astype(np.float32) @ k[:, h].astype(np.float32).T
+        assert np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs) < 1e-4
+
+
+def test_kv_v_path_is_quant_only():
+    cfg = synth.kv_config(T=8, H=2)
+    codes, s16, y = oracle.kv_quant(cfg["v"], rotate=False)
+    assert np.array_equal(y, cfg["v"].astype(np.float32))
+    c_ref, s_ref = oracle.quantize_kv_groups(y)
+    assert np.array_equal(oracle.unpack_int4(codes), c_ref) and np.array_equal(s16, s_ref)
+
+
+# ------------------------------------------------------------------ kurtosis
+
+def test_kurtosis_closed_forms():
+    # two-point +-1: m4 / m2^2 = 1
+    assert oracle.kurtosis_per_token(np.array([[1.0, -1.0] * 8]))[0] == pytest.approx(1.0)
+    # one spike c among n zeros (exact rational closed form)
+    n = 50
+    x = np.zeros((1, n))
+    x[0, 3] = 2.0
+    mu = Fraction(2, n)
+    vals = [Fraction(2) - mu] + [-mu] * (n - 1)
+    m2 = sum(v * v for v in vals) / n
+    m4 = sum(v ** 4 for v in vals) / n
+    assert oracle.kurtosis_per_token(x)[0] == pytest.approx(float(m4 / (m2 * m2)), rel=1e-12)
+    # Gaussian -> 3, uniform -> 1.8
+    rng = np.random.default_rng(0)
+    assert oracle.mean_kurtosis(rng.standard_normal((64, 20000))) == pytest.approx(3.0, abs=0.05)
+    assert oracle.mean_kurtosis(rng.random((64, 20000))) == pytest.approx(1.8, abs=0.02)
+
+
+def test_kurtosis_falls_to_about_three_after_rotation():
+    """Page "SpinQuant, Reproduced", Q3: kurtosis in the hundreds before rotation,
+    about 3 after.  Synthetic outlier activations (down_proj recipe, 256 tokens)."""
+    cfg = synth.down_config(M=256)
+    x = cfg["x"]
+    before = oracle.mean_kurtosis(x)
+    after_h = oracle.mean_kurtosis(oracle.rotate_rows(x, 12288))
+    assert before >= 50
+    assert 1.5 <= after_h <= 3.5
+    rng = np.random.default_rng(1)
+    r = synth.haar_orthogonal(rng, 1024)
+    xs = x[:, :1024].astype(np.float64)
+    xs[:, :2] *= 100.0
+    assert oracle.mean_kurtosis(xs) >= 50
+    assert 2.7 <= oracle.mean_kurtosis(xs @ r.astype(np.float64)) <= 3.3
