@@ -1,0 +1,236 @@
+"""Benchmark of the SpinQuant online hot path on one MI355X.
+
+One step = the R4 / down_proj path on a Qwen3-8B-shaped batch:
+    spin_fwht_quant  X [4096][12288] fp16 -> Hadamard 12288 (H_12 (x) H_1024)
+                     / sqrt(12288) -> per-token INT4 codes + scales
+    spin_w4a4_gemm   codes x INT4 weights [4096][12288] (Hadamard folded
+                     offline, untimed) -> Y [4096][4096] fp32
+Inputs are synthetic (seeded, 0.1% outlier channels x100) and resident in HBM
+before timing starts.  Several input / output buffer sets rotate so that each
+step reads activations that the 256 MB Infinity Cache no longer holds.
+
+Prints ONE JSON line.  `value` is fwht_quant's achieved GB/s (algorithmic
+bytes per launch / mean launch time, from HIP events on the launch stream);
+the GEMM's TOPS follow in `gemm_tops`; `roofline` describes the kernel that
+dominates the step (the GEMM) and `roofline_fwht_quant` the other one.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--gpus 1]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
+M, K, N, HAD_N = 4096, 12288, 4096, 12288
+FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
+KV_T, KV_H, KV_D = 4096, 32, 128
+KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
+
+# Traffic factors: measured HBM bytes per launch from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs, each scaled by the same counters read on a plain copy of
+# known size.  None until the counters have been taken on the current kernels.
+TRAFFIC_BYTES = {"w4a4_gemm": None, "fwht_quant": None}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold HBM)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    return ap.parse_args()
+
+
+def cpu_baseline(x_host):
+    """Time the oracle (untuned) on a bounded sample of the same workload."""
+    import oracle
+    from oracle import gemm as ogemm
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    rows_f = 2048
+    oracle.hadamard(HAD_N)                         # build H once, outside the timed region
+    t0 = time.perf_counter()
+    pk, s, _ = oracle.fwht_quant(x_host[:rows_f], HAD_N)
+    t_f = time.perf_counter() - t0
+    rows_g = 1024
+    qx = oracle.unpack_int4(pk[:rows_g])
+    # weight codes for the timing sample: seeded uniform codes of the workload's shape
+    wq_codes = np.random.default_rng(7).integers(-7, 8, size=(N, K)).astype(np.int8)
+    t0 = time.perf_counter()
+    ogemm.gemm_int_codes(qx, wq_codes)
+    t_g = time.perf_counter() - t0
+    omp = ogemm.num_threads()
+    return {
+        "value": rows_f * FWHT_BYTES_PER_TOKEN / t_f / 1e9,
+        "unit": "GB/s",
+        "cores": max(omp, blas_threads or 1),
+        "kind": "oracle",
+        "sample": (f"fwht_quant on {rows_f} of {M} tokens (dense float64 X.H_12288 + "
+                   f"float32 quantizer) in {t_f:.2f} s; int64 C GEMM on {rows_g} tokens x "
+                   f"{N} x {K} in {t_g:.2f} s"),
+        "gemm_tops": 2.0 * rows_g * N * K / t_g / 1e12,
+        "host_cpus": cores,
+        "blas_threads": blas_threads,
+        "omp_threads": omp,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the path shards by tokens with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    from rotation_bit_quantization_amd import spin, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    spin.load()
+
+    cfg = synth.down_config()
+    x_host, w_host = cfg["x"], cfg["w"]
+
+    # Offline fold (untimed): W' = (H_12288 / sqrt(12288))^T W, per-channel INT4.
+    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(w_host).to(dev), None, HAD_N)
+
+    sets = max(1, args.sets)
+    X = [torch.from_numpy(x_host).to(dev)]
+    for i in range(1, sets):                 # same values, distinct HBM buffers
+        X.append(X[0].clone())
+    Xq = [torch.empty((M, K // 2), dtype=torch.uint8, device=dev) for _ in range(sets)]
+    xs = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(sets)]
+    Y = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(sets)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        j = i % sets
+        if ev is not None:
+            ev[0].record(stream)
+        spin.spin_fwht_quant(X[j], HAD_N, Xq=Xq[j], x_scale=xs[j])
+        if ev is not None:
+            ev[1].record(stream)
+        spin.spin_w4a4_gemm(Xq[j], xs[j], Wq, ws, Y=Y[j])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    f_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    g_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    f_s, g_s = f_ms.mean() / 1e3, g_ms.mean() / 1e3
+    fwht_bytes = M * FWHT_BYTES_PER_TOKEN
+    fwht_gbps = fwht_bytes / f_s / 1e9
+    gemm_ops = 2.0 * M * N * K
+    gemm_tops = gemm_ops / g_s / 1e12
+
+    # Parity spot check of this run's output (first row of the last set) against the oracle.
+    j = (args.steps - 1) % sets
+    xq_row = Xq[j][:2].cpu().numpy()
+    pk, _, _ = oracle.fwht_quant(x_host[:2], HAD_N)
+    mism = float(np.mean(oracle.unpack_int4(xq_row) != oracle.unpack_int4(pk)))
+
+    extra = {}
+    if not args.no_kv:
+        kv = synth.kv_config()
+        Kd = [torch.from_numpy(kv["k"]).to(dev)] + [None] * (sets - 1)
+        for i in range(1, sets):
+            Kd[i] = Kd[0].clone()
+        kc = [torch.empty((KV_T, KV_H, KV_D // 2), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        ksc = [torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev) for _ in range(sets)]
+        for i in range(args.warmup):
+            spin.spin_kv_quant(Kd[i % sets], 1, codes=kc[i % sets], scale=ksc[i % sets])
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            kev[i][0].record(stream)
+            spin.spin_kv_quant(Kd[i % sets], 1, codes=kc[i % sets], scale=ksc[i % sets])
+            kev[i][1].record(stream)
+        torch.cuda.synchronize()
+        k_s = np.mean([e[0].elapsed_time(e[1]) for e in kev]) / 1e3
+        kv_bytes = KV_T * KV_H * KV_BYTES_PER_GROUP
+        extra["kv_quant"] = {"workload": "K [4096][32][128] fp16, H_128 + INT4, fp16 scale",
+                             "us": k_s * 1e6, "GBps": kv_bytes / k_s / 1e9,
+                             "frac_of_hbm": kv_bytes / k_s / 1e9 / HBM_PEAK_GBPS}
+        del Kd, kc, ksc
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = 1 << 30
+
+    line = {
+        "metric": "fwht_quant GB/s (% of 8 TB/s) + W4A4 GEMM TOPS (% INT8 MFMA peak), M=4096",
+        "value": round(fwht_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+i8",
+        "data": "synthetic (seeded N(0,1) activations, 0.1% channels x100; N(0,0.02) weights)",
+        "config": {"workload": "R4 down_proj path: fwht_quant X 4096x12288 fp16, had_n 12288 "
+                               "(H12 x H1024), per-token INT4; w4a4_gemm M=4096 N=4096 K=12288",
+                   "M": M, "K": K, "N": N, "had_n": HAD_N, "buffer_sets": sets},
+        "fwht_quant_us": round(f_s * 1e6, 3),
+        "fwht_quant_frac_of_hbm": round(fwht_gbps / HBM_PEAK_GBPS, 4),
+        "gemm_us": round(g_s * 1e6, 3),
+        "gemm_tops": round(gemm_tops, 2),
+        "gemm_frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
+        "roofline": {"kernel": "w4a4_gemm", "bound": "mfma", "achieved": round(gemm_tops, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": TRAFFIC_BYTES["w4a4_gemm"]},
+        "roofline_fwht_quant": {"kernel": "fwht_quant", "bound": "hbm", "achieved": round(fwht_gbps, 2),
+                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": round(fwht_gbps / HBM_PEAK_GBPS, 4),
+                                "traffic": TRAFFIC_BYTES["fwht_quant"]},
+        "parity_spot_code_mismatch": mism,
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x_host)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,8 @@ The rotation is a dense float64 product (``x @ H``), divided by sqrt(n) in
 float64, and the caller rounds the float64 result once to float32.
 """
 
+import functools
+
 import numpy as np
 
 __all__ = ["sylvester", "paley12", "hadamard", "rotate_rows", "supported_had_n"]
@@ -83,15 +85,19 @@ def supported_had_n(n: int) -> bool:
     return False
 
 
+@functools.lru_cache(maxsize=8)
 def hadamard(n: int) -> np.ndarray:
-    """Unnormalised Hadamard matrix of order n used by the library (int64)."""
+    """Unnormalised Hadamard matrix of order n used by the library (int64, read-only)."""
     if not supported_had_n(n):
         raise ValueError(f"unsupported Hadamard order {n}")
     if n == 1:
-        return np.ones((1, 1), dtype=np.int64)
-    if (n & (n - 1)) == 0:
-        return sylvester(n)
-    return np.kron(paley12(), sylvester(n // 12))
+        h = np.ones((1, 1), dtype=np.int64)
+    elif (n & (n - 1)) == 0:
+        h = sylvester(n)
+    else:
+        h = np.kron(paley12(), sylvester(n // 12))
+    h.setflags(write=False)
+    return h
 
 
 def rotate_rows(x, n: int) -> np.ndarray:

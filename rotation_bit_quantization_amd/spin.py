@@ -1,0 +1,190 @@
+"""Thin Python binding of the libspin C ABI (ctypes; argument marshalling only).
+
+Every function here checks tensor dtype / device / contiguity, allocates the
+outputs it was not given (torch device memory), and calls the C entry point
+of the same name on torch's current HIP stream.  All arithmetic happens in the
+HIP kernels of libspin.so; if the library is missing this module raises
+instead of computing anything itself.
+
+Declarations and contracts: include/libspin.h.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
+           "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
+           "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
+           "spin_w4a4_gemm", "spin_kv_quant", "EXPORTED_SYMBOLS"]
+
+SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
+    SPIN_ERR_HIP = range(6)
+SPIN_F32, SPIN_F16 = 0, 1
+
+EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
+                    "spin_status_string", "spin_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libspin.so")
+
+
+class SpinError(RuntimeError):
+    """A libspin call returned a non-zero spin_status."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {spin_status_string(status)}")
+
+
+def load():
+    """Load libspin.so (raises OSError with a build hint if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with `python -m rotation_bit_quantization_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.spin_fold_rotation.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp]
+    lib.spin_fwht_quant.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+    lib.spin_w4a4_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
+    for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.spin_status_string.argtypes = [ctypes.c_int]
+    lib.spin_status_string.restype = ctypes.c_char_p
+    lib.spin_version.argtypes = []
+    lib.spin_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def spin_status_string(status: int) -> str:
+    return load().spin_status_string(int(status)).decode()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn, status):
+    if status != SPIN_OK:
+        raise SpinError(fn, status)
+
+
+def _dtype_code(t):
+    return SPIN_F16 if t.dtype == torch.float16 else SPIN_F32
+
+
+def spin_fold_rotation(W, R, r_block, W_rot=None, Wq=None, w_scale=None, stream=None):
+    """W [K, N] fp32, R [r, r] fp32 or None -> (W_rot [K, N] fp32, Wq [N, K/2] u8, w_scale [N] fp32)."""
+    _check(W, "W", (torch.float32,))
+    K, N = W.shape
+    if R is not None:
+        _check(R, "R", (torch.float32,), (r_block, r_block))
+    dev = W.device
+    W_rot = torch.empty((K, N), dtype=torch.float32, device=dev) if W_rot is None else W_rot
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev) if Wq is None else Wq
+    w_scale = torch.empty((N,), dtype=torch.float32, device=dev) if w_scale is None else w_scale
+    _check(W_rot, "W_rot", (torch.float32,), (K, N))
+    _check(Wq, "Wq", (torch.uint8,), (N, K // 2))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    st = load().spin_fold_rotation(_ptr(W), K, N, _ptr(R), int(r_block), _ptr(W_rot), _ptr(Wq),
+                                   _ptr(w_scale), _stream(stream))
+    _raise("spin_fold_rotation", st)
+    return W_rot, Wq, w_scale
+
+
+def spin_fwht_quant(X, had_n, Xq=None, x_scale=None, X_rot=None, want_rot=False, stream=None):
+    """X [M, K] fp16/fp32 -> (Xq [M, K/2] u8, x_scale [M] fp32, X_rot [M, K] fp32 or None)."""
+    _check(X, "X", (torch.float16, torch.float32))
+    M, K = X.shape
+    dev = X.device
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if Xq is None else Xq
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    if X_rot is None and want_rot:
+        X_rot = torch.empty((M, K), dtype=torch.float32, device=dev)
+    _check(Xq, "Xq", (torch.uint8,), (M, K // 2))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    if X_rot is not None:
+        _check(X_rot, "X_rot", (torch.float32,), (M, K))
+    st = load().spin_fwht_quant(_ptr(X), _dtype_code(X), M, K, int(had_n), _ptr(Xq), _ptr(x_scale),
+                                _ptr(X_rot), _stream(stream))
+    _raise("spin_fwht_quant", st)
+    return Xq, x_scale, X_rot
+
+
+def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=False, stream=None):
+    """Packed Xq [M, K/2], Wq [N, K/2] + scales -> (Y [M, N] fp32, acc [M, N] int32 or None)."""
+    _check(Xq, "Xq", (torch.uint8,))
+    _check(Wq, "Wq", (torch.uint8,))
+    M, Kh = Xq.shape
+    N, Kh2 = Wq.shape
+    if Kh != Kh2:
+        raise ValueError("Xq and Wq disagree on K")
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    dev = Xq.device
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev) if Y is None else Y
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    st = load().spin_w4a4_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, 2 * Kh,
+                               _ptr(Y), _ptr(acc_out), _stream(stream))
+    _raise("spin_w4a4_gemm", st)
+    return Y, acc_out
+
+
+def spin_kv_quant(X, rotate, quantize=True, codes=None, scale=None, X_rot=None, want_rot=False,
+                  stream=None):
+    """X [T, H, 128] fp16/fp32 -> (codes [T, H, 64] u8 | None, scale [T, H] fp16 | None, X_rot | None).
+
+    ``scale`` is returned as a float16 tensor holding the fp16 bit patterns the
+    library writes.
+    """
+    _check(X, "X", (torch.float16, torch.float32))
+    T, H, D = X.shape
+    dev = X.device
+    if quantize:
+        codes = torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+        scale = torch.empty((T, H), dtype=torch.float16, device=dev) if scale is None else scale
+        _check(codes, "codes", (torch.uint8,), (T, H, D // 2))
+        _check(scale, "scale", (torch.float16,), (T, H))
+    if X_rot is None and (want_rot or not quantize):
+        X_rot = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    if X_rot is not None:
+        _check(X_rot, "X_rot", (torch.float32,), (T, H, D))
+    st = load().spin_kv_quant(_ptr(X), _dtype_code(X), T, H, D, int(rotate), _ptr(codes),
+                              _ptr(scale), _ptr(X_rot), _stream(stream))
+    _raise("spin_kv_quant", st)
+    return codes, scale, X_rot

@@ -1,0 +1,313 @@
+"""GPU parity: libspin (through its C ABI) against the CPU oracle.
+
+Acceptance, per operation:
+  * rotated float32 values (X_rot, W_rot) within 1e-5 relative of the oracle's
+    float64 product, per row: ||d||_2 <= 1e-5 ||ref||_2 and
+    max |d| <= 1e-5 max |ref|;
+  * codes and scales bit-exact with the oracle quantizer applied to the GPU's
+    own float32 rotated values (float32 decides the integer on both sides);
+  * int32 accumulators bit-exact with the oracle's int64 GEMM;
+  * final float32 outputs within 1e-3 relative of the oracle end to end, and
+    bit-exact with the oracle epilogue applied to the GPU's accumulators.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rotation_bit_quantization_amd import spin, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spin.load()
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_rows_close(got, ref, tol=1e-5):
+    got = np.asarray(got, np.float64).reshape(-1, np.shape(got)[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    d = got - ref
+    nref = np.linalg.norm(ref, axis=1)
+    assert (np.linalg.norm(d, axis=1) <= tol * nref + 1e-30).all(), \
+        f"normwise rel err {np.max(np.linalg.norm(d, axis=1) / np.maximum(nref, 1e-30)):.3g}"
+    assert (np.abs(d).max(axis=1) <= tol * np.abs(ref).max(axis=1) + 1e-30).all(), \
+        f"max abs err {np.abs(d).max():.3g}"
+
+
+def assert_y_close(got, ref, tol=1e-3, flip_rows=(), flip_cols=()):
+    """Final outputs against the oracle's own end-to-end chain: per row
+    ||d||_2 <= tol ||ref||_2, and |d| <= tol (|ref| + rms_row(ref)) for every
+    element except those whose row or column holds a code that legitimately
+    differs at a near-tie (the oracle rounds its float64 rotation, the GPU its
+    float32 one); such flips are passed in and must themselves be rare."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    assert (np.linalg.norm(d, axis=1) <= tol * np.linalg.norm(ref, axis=1) + 1e-30).all()
+    bad = np.abs(d) > tol * (np.abs(ref) + rms) + 1e-30
+    explained = np.zeros_like(bad)
+    explained[list(flip_rows), :] = True
+    explained[:, list(flip_cols)] = True
+    assert not (bad & ~explained).any(), f"{int((bad & ~explained).sum())} unexplained outliers"
+
+
+def code_flips(gpu_packed, ref_packed, axis):
+    """Indices (rows of a [R][K/2] code matrix) where GPU and oracle codes differ."""
+    g = oracle.unpack_int4(gpu_packed)
+    r = oracle.unpack_int4(ref_packed)
+    diff = g != r
+    assert diff.mean() < 1e-4, f"code mismatch rate {diff.mean()}"
+    return np.nonzero(diff.any(axis=axis))[0]
+
+
+def check_fwht_quant(x, had_n, rows=None):
+    """Run spin_fwht_quant on x; check against the oracle on `rows` (all if None)."""
+    X = _dev(x)
+    Xq, xs, Xr = spin.spin_fwht_quant(X, had_n, want_rot=True)
+    Xq2, xs2, _ = spin.spin_fwht_quant(X, had_n)                 # no X_rot: same codes
+    xq, s, xr = _host(Xq), _host(xs), _host(Xr)
+    assert np.array_equal(xq, _host(Xq2)) and np.array_equal(s, _host(xs2))
+    # codes / scales: bit-exact with the oracle quantizer on the GPU's own y (all rows)
+    c_ref, s_ref = oracle.quantize_rows(xr)
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(xq, oracle.pack_int4(c_ref))
+    # y against the oracle's float64 rotation (sampled rows at large sizes)
+    sel = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    pk, s_o, y_o = oracle.fwht_quant(x[sel], had_n)
+    assert_rows_close(xr[sel], y_o)
+    mism = np.mean(oracle.unpack_int4(xq[sel]) != oracle.unpack_int4(pk))
+    assert mism < 1e-4, f"direct code mismatch rate {mism}"
+    return xq, s, xr
+
+
+# ---------------------------------------------------------------- fwht_quant
+
+def test_fwht_quant_tiny_config():
+    cfg = synth.tiny_config()
+    check_fwht_quant(cfg["x"], cfg["had_n"])
+
+
+@pytest.mark.parametrize("had_n,K", [(1, 96), (2, 64), (16, 256), (128, 4096), (256, 768),
+                                     (1024, 2048), (4096, 4096), (16384, 16384), (12, 96),
+                                     (24, 480), (96, 192), (192, 3072), (3072, 6144),
+                                     (12288, 12288), (12288, 24576)])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_fwht_quant_orders(had_n, K, dtype):
+    rng = np.random.default_rng(had_n * 7 + K)
+    M = 37
+    x, _ = synth.outlier_activations(rng, M, K, max(1, K // 1000), 100.0, dtype=dtype)
+    check_fwht_quant(x, had_n)
+
+
+def test_fwht_quant_zero_and_tiny_rows():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((6, 12288)).astype(np.float16)
+    x[1] = 0
+    x[3] = 0
+    x[3, 100] = np.float16(6e-8)                                 # fp16 subnormal
+    xq, s, _ = check_fwht_quant(x, 12288)
+    assert s[1] == 0 and (xq[1] == 0).all()
+
+
+def test_fwht_quant_down_config_full_size():
+    cfg = synth.down_config()
+    rows = np.array([0, 1, 511, 2048, 4095])
+    check_fwht_quant(cfg["x"], cfg["had_n"], rows=rows)
+
+
+# ---------------------------------------------------------------- kv_quant
+
+def check_kv(x, rotate, groups=None):
+    X = _dev(x)
+    codes, s16, xr = spin.spin_kv_quant(X, rotate, want_rot=True)
+    c, s, y = _host(codes), _host(s16), _host(xr)
+    c_ref, s_ref = oracle.quantize_kv_groups(y)
+    assert np.array_equal(s.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c, oracle.pack_int4(c_ref))
+    T, H, D = x.shape
+    flat = x.reshape(T * H, 1, D)
+    sel = np.arange(T * H) if groups is None else np.asarray(groups)
+    _, _, y_o = oracle.kv_quant(flat[sel], rotate=bool(rotate))
+    assert_rows_close(y.reshape(T * H, D)[sel], y_o.reshape(-1, D))
+    # rotate-only (Q path) gives the same y
+    _, _, xr2 = spin.spin_kv_quant(X, rotate, quantize=False)
+    assert np.array_equal(_host(xr2), y)
+    return c, s, y
+
+
+@pytest.mark.parametrize("rotate", [1, 0])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_kv_quant_small(rotate, dtype):
+    cfg = synth.kv_config(T=33, H=5)
+    check_kv(cfg["k"].astype(dtype), rotate)
+
+
+def test_kv_quant_full_size_and_qk_invariance():
+    cfg = synth.kv_config()
+    rng = np.random.default_rng(3)
+    groups = rng.choice(4096 * 32, 2048, replace=False)
+    _, _, k_rot = check_kv(cfg["k"], 1, groups)
+    _, _, q_rot = spin.spin_kv_quant(_dev(cfg["q"]), 1, quantize=False)
+    q_rot = _host(q_rot)
+    t = np.arange(0, 4096, 8)
+    for h in (0, 17, 31):
+        lhs = q_rot[t, h] @ k_rot[t, h].T
+        rhs = cfg["q"][t, h].astype(np.float32) @ cfg["k"][t, h].astype(np.float32).T
+        assert np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs) < 1e-4
+    check_kv(cfg["v"][:512], 0)
+
+
+# ---------------------------------------------------------------- fold
+
+def check_fold(w, r, r_block, cols=None):
+    Wd = _dev(w)
+    Rd = None if r is None else _dev(r)
+    W_rot, Wq, ws = spin.spin_fold_rotation(Wd, Rd, r_block)
+    wr, wq, s = _host(W_rot), _host(Wq), _host(ws)
+    c_ref, s_ref = oracle.quantize_rows(wr.T)
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(wq, oracle.pack_int4(c_ref))
+    sel = np.arange(w.shape[1]) if cols is None else np.asarray(cols)
+    ref, _, _ = oracle.fold_rotation(w[:, sel], r, r_block)
+    assert_rows_close(wr[:, sel].T, ref.T)
+    return wr, wq, s
+
+
+def test_fold_tiny_haar():
+    cfg = synth.tiny_config()
+    check_fold(cfg["w"], cfg["r"], 256)
+
+
+@pytest.mark.parametrize("r_block,K,N", [(256, 256, 40), (12, 192, 17), (96, 384, 33),
+                                         (128, 4096, 70), (12288, 12288, 24), (1, 64, 5),
+                                         (64, 128, 65)])
+def test_fold_hadamard_orders(r_block, K, N):
+    rng = np.random.default_rng(r_block + K)
+    w = synth.gaussian_weight(rng, K, N)
+    check_fold(w, None, r_block)
+
+
+def test_fold_head_wise_r2():
+    rng = np.random.default_rng(21)
+    w = synth.gaussian_weight(rng, 4096, 96)
+    r2 = synth.haar_orthogonal(rng, 128)
+    check_fold(w, r2, 128)
+
+
+def test_fold_qkv_config_r1_full_size_sampled():
+    cfg = synth.qkv_config()
+    check_fold(cfg["w"], cfg["r"], 4096, cols=np.arange(0, 6144, 97))
+
+
+# ---------------------------------------------------------------- gemm
+
+def check_gemm(qx, qw, sx, sw, rows=None):
+    Xq, Wq = _dev(oracle.pack_int4(qx)), _dev(oracle.pack_int4(qw))
+    Y, acc = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw), want_acc=True)
+    Y2, _ = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw))
+    y, a = _host(Y), _host(acc)
+    assert np.array_equal(y, _host(Y2))
+    sel = np.arange(qx.shape[0]) if rows is None else np.asarray(rows)
+    a_ref = oracle.gemm_rows(qx, qw, sel)
+    assert np.array_equal(a[sel].astype(np.int64), a_ref)
+    assert np.array_equal(y[sel], oracle.dequant(a_ref, sx[sel], sw))
+    return y, a
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (37, 53, 128), (130, 260, 256), (128, 128, 4096),
+                                   (300, 200, 12288), (16, 4096, 4096), (129, 7, 192)])
+def test_gemm_ragged(M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw)
+
+
+def test_gemm_extreme_accumulators():
+    K = 12288
+    qx = np.full((3, K), 7, np.int8)
+    qx[1] = -7
+    qx[2, ::2] = -8                                              # -8 nibbles are accepted
+    qw = np.full((2, K), -7, np.int8)
+    qw[1] = 7
+    _, a = check_gemm(qx, qw, np.ones(3, np.float32), np.ones(2, np.float32))
+    assert a[0, 0] == -49 * K and a[1, 0] == 49 * K
+
+
+def test_gemm_down_config_shape_sampled():
+    rng = np.random.default_rng(22)
+    M, N, K = 4096, 4096, 12288
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw, rows=[0, 1, 127, 128, 2047, 4095])
+
+
+# ---------------------------------------------------------------- end to end
+
+def test_tiny_chain_end_to_end():
+    """Tiny workload, both chains: (i) Hadamard on X, W folded with H_256;
+    (ii) X rotated by R upstream, W folded with R."""
+    cfg = synth.tiny_config()
+    x, w, r = cfg["x"], cfg["w"], cfg["r"]
+    # (i)
+    Xq, xs, _ = spin.spin_fwht_quant(_dev(x), 256)
+    _, Wq, ws = spin.spin_fold_rotation(_dev(w), None, 256)
+    Y, _ = spin.spin_w4a4_gemm(Xq, xs, Wq, ws)
+    pk, s_o, _ = oracle.fwht_quant(x, 256)
+    _, wq_o, ws_o = oracle.fold_rotation(w, None, 256)
+    y_o, _ = oracle.w4a4_gemm(pk, s_o, wq_o, ws_o)
+    assert_y_close(_host(Y), y_o)
+    # (ii)
+    xr = (x.astype(np.float64) @ r.astype(np.float64)).astype(np.float32)
+    Xq, xs, _ = spin.spin_fwht_quant(_dev(xr), 1)
+    _, Wq, ws = spin.spin_fold_rotation(_dev(w), _dev(r), 256)
+    Y, _ = spin.spin_w4a4_gemm(Xq, xs, Wq, ws)
+    pk, s_o, _ = oracle.fwht_quant(xr, 1)
+    _, wq_o, ws_o = oracle.fold_rotation(w, r, 256)
+    y_o, _ = oracle.w4a4_gemm(pk, s_o, wq_o, ws_o)
+    assert_y_close(_host(Y), y_o)
+
+
+def test_down_chain_end_to_end_sampled():
+    cfg = synth.down_config()
+    x, w = cfg["x"], cfg["w"]
+    Xq, xs, _ = spin.spin_fwht_quant(_dev(x), 12288)
+    _, Wq, ws = spin.spin_fold_rotation(_dev(w), None, 12288)
+    Y, acc = spin.spin_w4a4_gemm(Xq, xs, Wq, ws, want_acc=True)
+    rows = np.array([0, 777, 4095])
+    cols = np.arange(0, 4096, 64)
+    pk, s_o, _ = oracle.fwht_quant(x[rows], 12288)
+    _, wq_o, ws_o = oracle.fold_rotation(w[:, cols], None, 12288)
+    a_o = oracle.gemm_rows(oracle.unpack_int4(pk), oracle.unpack_int4(wq_o), np.arange(3))
+    y_o = oracle.dequant(a_o, s_o, ws_o)
+    fr = code_flips(_host(Xq)[rows], pk, axis=1)
+    fc = code_flips(_host(Wq)[cols], wq_o, axis=1)
+    assert_y_close(_host(Y)[rows][:, cols], y_o, flip_rows=fr, flip_cols=fc)
+
+
+def test_repeat_runs_are_deterministic():
+    cfg = synth.down_config(M=256)
+    X = _dev(cfg["x"])
+    a = [_host(spin.spin_fwht_quant(X, 12288)[0]) for _ in range(3)]
+    assert all(np.array_equal(a[0], b) for b in a[1:])
