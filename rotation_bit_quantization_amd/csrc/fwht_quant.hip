@@ -84,6 +84,174 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
     }
 }
 
+// ---------------------------------------------------------------------------
+// fwht_quant_k12288: the R4 / down_proj case, fp16 rows of 12288 = 12 x 1024
+// with had_n = 12288.  Element i = a * 1024 + b; the transform is
+// Y = H12^T X H1024 on the 12 x 1024 view (x . (H12 (x) H1024)).
+//
+// One workgroup of 256 threads per row, two register layouts and one LDS
+// exchange:
+//   phase 1  thread holds x[a][4 beta + j] for all 12 a and j = 0..3
+//            (twelve 8-byte loads).  b bits 0-1 are butterflied in registers,
+//            the H12 mix runs in registers, b bits 2-5 are the low lane bits
+//            (four DPP levels); b bits 6-7 are lane bits 4-5, b bits 8-9 the
+//            wave.
+//   LDS      the rotated values are written in natural order, 64-float rows
+//            padded to 68 so that the phase-2 reads spread over the banks.
+//   phase 2  thread holds 8 consecutive b (bits 0-2) for 6 of the 12 a: b bits
+//            6-9 are the low lane bits (four more DPP levels), b bits 3-4 lane
+//            bits 4-5, b bit 5 wave bit 0, the half of a wave bit 1.
+// Each DPP stage leaves lane i with (-1)^popcount(i & 7) times its value; both
+// signs, and nothing else, are folded into the per-thread quantizer constant.
+// The absmax is a block reduction; codes come from the magic-number quantizer
+// with an exact fallback near ties, eight per dword store.
+constexpr int kLdsRowF = 68;                 // 64 floats + 4 pad
+constexpr int kLdsAF = 16 * kLdsRowF;        // one a (1024 b) = 16 padded rows
+constexpr int kLdsFloats12288 = 12 * kLdsAF;
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
+}
+
+template <bool WRITE_ROT>
+__global__ __launch_bounds__(256) void fwht_quant_k12288(
+    const __half* __restrict__ X, float norm, uint8_t* __restrict__ Xq,
+    float* __restrict__ x_scale, float* __restrict__ X_rot) {
+    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats12288];
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l16 = lane & 15;
+    const size_t row = blockIdx.x;
+    const __half* xr = X + row * 12288;
+
+    const float s1 = lane_sign(l16, 0b0101), s2 = lane_sign(l16, 0b0110);
+    const float s3 = lane_sign(l16, 0b1100), s4 = lane_sign(l16, 0b1000);
+
+    // ---- phase 1: load x[a][4 beta .. 4 beta + 3], beta bits 0-3 permuted for DPP
+    const int beta_in = g_perm(l16) | ((lane >> 4) << 4) | (wave << 6);
+    uint2 raw[12];
+#pragma unroll
+    for (int a = 0; a < 12; ++a)
+        raw[a] = *reinterpret_cast<const uint2*>(xr + a * 1024 + 4 * beta_in);
+
+    float v[12][4];
+#pragma unroll
+    for (int a = 0; a < 12; ++a) {
+        const float x0 = h2f_lo(raw[a].x), x1 = h2f_hi(raw[a].x);
+        const float x2 = h2f_lo(raw[a].y), x3 = h2f_hi(raw[a].y);
+        const float s01 = x0 + x1, d01 = x0 - x1, s23 = x2 + x3, d23 = x2 - x3;
+        v[a][0] = s01 + s23;
+        v[a][1] = d01 + d23;
+        v[a][2] = s01 - s23;
+        v[a][3] = d01 - d23;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float col[12];
+#pragma unroll
+        for (int a = 0; a < 12; ++a) col[a] = v[a][j];
+        h12_row(col);
+#pragma unroll
+        for (int a = 0; a < 12; ++a) v[a][j] = col[a];
+    }
+    dpp_wht16<48>(&v[0][0], s1, s2, s3, s4);
+
+    // ---- exchange: lane i now holds natural b bits 2-5 = i
+    {
+        const int beta = l16 | ((lane >> 4) << 4) | (wave << 6);
+        float* dst = lds + (beta >> 4) * kLdsRowF + 4 * l16;
+#pragma unroll
+        for (int c = 0; c < 12; ++c)
+            *reinterpret_cast<float4*>(dst + c * kLdsAF) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
+    }
+    __syncthreads();
+
+    // ---- phase 2: 8 consecutive b of 6 rows c of the 12 x 1024 view
+    const int ch = wave >> 1;
+    const int blo = 8 * (((lane >> 4) & 3) | ((wave & 1) << 2));      // b & 63
+    float z[6][8];
+    {
+        const float* src = lds + g_perm(l16) * kLdsRowF + blo + ch * 6 * kLdsAF;
+#pragma unroll
+        for (int ci = 0; ci < 6; ++ci) {
+            const float4 p = *reinterpret_cast<const float4*>(src + ci * kLdsAF);
+            const float4 q = *reinterpret_cast<const float4*>(src + ci * kLdsAF + 4);
+            z[ci][0] = p.x; z[ci][1] = p.y; z[ci][2] = p.z; z[ci][3] = p.w;
+            z[ci][4] = q.x; z[ci][5] = q.y; z[ci][6] = q.z; z[ci][7] = q.w;
+        }
+    }
+    dpp_wht16<48>(&z[0][0], s1, s2, s3, s4);
+
+    // ---- absmax of the row
+    float mx = 0.0f;
+#pragma unroll
+    for (int ci = 0; ci < 6; ++ci)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(z[ci][k]));
+    const float amax = block_max_256(mx, red) * norm;   // = max_i fl32(|z_i| * norm)
+    const float s = __fdiv_rn(amax, kSeven);
+    if (tid == 0) x_scale[row] = s;
+
+    // Sign of each held value relative to the true transform: phase 1 left
+    // (-1)^popcount(b2..b4), phase 2 (-1)^popcount(b6..b8) (b2 = register bit 2).
+    const int b3 = (lane >> 4) & 1, b4 = (lane >> 5) & 1;
+    const bool neg_lo = ((b3 ^ b4) ^ (__builtin_popcount(l16 & 7) & 1)) != 0;
+    const float sg_lo = neg_lo ? -1.0f : 1.0f;        // registers k = 0..3 (b2 = 0)
+    const float sg_hi = -sg_lo;                        // registers k = 4..7 (b2 = 1)
+
+    const size_t obase = row * 6144 + (ch * 6) * 512 + (l16 * 64 + blo) / 2;
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + obase);
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    if (fast) {
+        const float cr = norm * __fdiv_rn(1.0f, s);
+        const float cr_lo = sg_lo * cr, cr_hi = sg_hi * cr;
+#pragma unroll
+        for (int ci = 0; ci < 6; ++ci) {
+            uint32_t f[8];
+            bool tie = false;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                f[k] = __float_as_uint(__builtin_fmaf(z[ci][k], k < 4 ? cr_lo : cr_hi, kQuantMagic));
+                tie |= near_tie(f[k]);
+            }
+            uint32_t word = pack8_magic(f);
+            if (tie) {
+                int c8[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    c8[k] = quant_exact((z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm, s);
+                word = pack8(c8);
+            }
+            out[ci * 128] = word;
+        }
+    } else {
+#pragma unroll
+        for (int ci = 0; ci < 6; ++ci) {
+            int c8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                c8[k] = quant_exact((z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm, s);
+            out[ci * 128] = pack8(c8);
+        }
+    }
+    if (WRITE_ROT) {
+        float* yr = X_rot + row * 12288 + (ch * 6) * 1024 + l16 * 64 + blo;
+#pragma unroll
+        for (int ci = 0; ci < 6; ++ci) {
+            float y[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) y[k] = (z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm;
+            *reinterpret_cast<float4*>(yr + ci * 1024) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4*>(yr + ci * 1024 + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        }
+    }
+}
+
 template <typename TIn, bool WR>
 hipError_t launch_rowlds(const TIn* X, int M, int K, HadOrder h, uint8_t* Xq, float* xs,
                          float* Xr, hipStream_t s) {
@@ -102,6 +270,17 @@ hipError_t launch_rowlds(const TIn* X, int M, int K, HadOrder h, uint8_t* Xq, fl
 
 hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h, uint8_t* Xq,
                              float* x_scale, float* X_rot, hipStream_t s) {
+    if (x_f16 && h.n == 12288 && K == 12288) {
+        const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
+        const __half* x = static_cast<const __half*>(X);
+        if (X_rot)
+            hipLaunchKernelGGL((fwht_quant_k12288<true>), dim3(M), dim3(256), 0, s, x, norm, Xq,
+                               x_scale, X_rot);
+        else
+            hipLaunchKernelGGL((fwht_quant_k12288<false>), dim3(M), dim3(256), 0, s, x, norm, Xq,
+                               x_scale, X_rot);
+        return hipGetLastError();
+    }
     if (x_f16) {
         const __half* x = static_cast<const __half*>(X);
         return X_rot ? launch_rowlds<__half, true>(x, M, K, h, Xq, x_scale, X_rot, s)

@@ -89,3 +89,137 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
 }
 
 }  // namespace spin
+
+namespace spin {
+
+// y = x . H12 (Paley-I, unnormalised) for a row vector of 12, in place.
+//
+// Every order-12 Hadamard matrix is equivalent to every other under signed
+// row and column permutations.  Paley's second construction over GF(5) has
+// the block form H' = [[C + I, C - I], [C - I, -C - I]] with C the symmetric
+// order-6 conference matrix C = [[0, 1^T], [1, Q5]], Q5[a][b] = chi5(b - a)
+// (chi5 = +1 at +-1, -1 at +-2).  Our H12 = P H' S with P, S signed
+// permutations (found offline by matching the two matrices row by row), so
+// x . H12 = ((x . P) . H') . S.  With u = x . P split as [u1 | u2]:
+//   w1 = (u1 + u2) C + (u1 - u2),   w2 = (u1 - u2) C - (u1 + u2),
+// and the product of a 6-vector A with C needs, with A' = A[1..5] and
+// p_b = A'[b+1] + A'[b-1], S = sum A':  (A C)[0] = S and
+// (A C)[1+b] = A[0] - S + A'[b] + 2 p_b.  Folding the + (u1 - u2) and
+// - (u1 + u2) terms in gives w1[1+b] = (U0 - S_U) + 2 (p_b(U) + u1[1+b]) and
+// w2[1+b] = (V0 - S_V) + 2 (p_b(V) - u2[1+b]).  50 adds / FMAs for 12 outputs
+// instead of 132.
+__device__ __forceinline__ void h12_row(float (&x)[12]) {
+    // u = x . P  (input permutation and signs)
+    const float u0 = x[0], u1 = x[1], u2 = x[2], u3 = -x[3], u4 = -x[5], u5 = -x[7];
+    const float u6 = -x[9], u7 = x[4], u8 = x[8], u9 = -x[6], u10 = x[10], u11 = -x[11];
+    const float U0 = u0 + u6, U1 = u1 + u7, U2 = u2 + u8, U3 = u3 + u9, U4 = u4 + u10, U5 = u5 + u11;
+    const float V0 = u0 - u6, V1 = u1 - u7, V2 = u2 - u8, V3 = u3 - u9, V4 = u4 - u10, V5 = u5 - u11;
+    // p_b over the five non-border entries, indices mod 5
+    const float P0 = U2 + U5, P1 = U3 + U1, P2 = U4 + U2, P3 = U5 + U3, P4 = U1 + U4;
+    const float SU = P0 + P1 + U4;
+    const float EU = U0 - SU;
+    const float Q0 = V2 + V5, Q1 = V3 + V1, Q2 = V4 + V2, Q3 = V5 + V3, Q4 = V1 + V4;
+    const float SV = Q0 + Q1 + V4;
+    const float EV = V0 - SV;
+    const float w0 = SU + V0;
+    const float w1 = __builtin_fmaf(2.0f, P0 + u1, EU);
+    const float w2 = __builtin_fmaf(2.0f, P1 + u2, EU);
+    const float w3 = __builtin_fmaf(2.0f, P2 + u3, EU);
+    const float w4 = __builtin_fmaf(2.0f, P3 + u4, EU);
+    const float w5 = __builtin_fmaf(2.0f, P4 + u5, EU);
+    const float w6 = SV - U0;
+    const float w7 = __builtin_fmaf(2.0f, Q0 - u7, EV);
+    const float w8 = __builtin_fmaf(2.0f, Q1 - u8, EV);
+    const float w9 = __builtin_fmaf(2.0f, Q2 - u9, EV);
+    const float w10 = __builtin_fmaf(2.0f, Q3 - u10, EV);
+    const float w11 = __builtin_fmaf(2.0f, Q4 - u11, EV);
+    // y = w . S  (output permutation and signs)
+    x[0] = w4;  x[1] = w11; x[2] = w0;  x[3] = w7;  x[4] = w5;   x[5] = w2;
+    x[6] = w1;  x[7] = w9;  x[8] = -w6; x[9] = w10; x[10] = w8;  x[11] = w3;
+}
+
+}  // namespace spin
+
+namespace spin {
+
+// One butterfly level across the 16 lanes of a DPP row, for eight registers:
+// r[i] <- r[i] + sgn * r[i] of the partner lane, as a single v_fmac_f32 with a
+// DPP source operand.  `sgn` is +1 on the lane of each pair that keeps the sum
+// and -1 on the other, which leaves the latter with -(partner - self); the
+// sign is carried and removed once at the end.  The partner patterns used are
+// quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane ^ 7) and row_mirror (lane ^ 15).  A VALU write of a
+// VGPR must be two wait states ahead of a DPP read of it, hence the s_nop.
+#define SPIN_DPP_FMAC8(CTRL, r, s)                                                    \
+    asm("s_nop 1\n\t"                                                                  \
+        "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"            \
+        "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                \
+        : "+v"((r)[0]), "+v"((r)[1]), "+v"((r)[2]), "+v"((r)[3]), "+v"((r)[4]),        \
+          "+v"((r)[5]), "+v"((r)[6]), "+v"((r)[7])                                     \
+        : "v"(s))
+
+#define SPIN_DPP_XOR1 "quad_perm:[1,0,3,2]"
+#define SPIN_DPP_XOR2 "quad_perm:[2,3,0,1]"
+#define SPIN_DPP_XOR7 "row_half_mirror"
+#define SPIN_DPP_XOR15 "row_mirror"
+
+// Butterflies along the lane masks 1, 2, 7, 15 realise a Walsh-Hadamard
+// transform over the four low lane bits in the coordinates of the dual basis
+// phi = {0b0101, 0b0110, 0b1100, 0b1000}: lane i takes sign (-1)^<i, phi_k> at
+// level k.  If lane i first holds element g_perm(i) of a 16-point row, lane i
+// ends holding element i of its natural-order transform multiplied by
+// (-1)^popcount(i & 7).  g_perm is the Gram matrix sum_k phi_k phi_k^T over
+// GF(2) acting on the lane bits.
+__device__ __forceinline__ int g_perm(int i) {
+    const int i0 = i & 1, i1 = (i >> 1) & 1, i2 = (i >> 2) & 1, i3 = (i >> 3) & 1;
+    return (i0 ^ i2) | ((i1 ^ i2) << 1) | ((i0 ^ i1 ^ i2 ^ i3) << 2) | (i2 << 3);
+}
+
+__device__ __forceinline__ float lane_sign(int l16, int phi) {
+    return (__builtin_popcount(l16 & phi) & 1) ? -1.0f : 1.0f;
+}
+
+// Four DPP levels over n registers (n a multiple of 8).
+template <int NREG>
+__device__ __forceinline__ void dpp_wht16(float* r, float s1, float s2, float s3, float s4) {
+#pragma unroll
+    for (int i = 0; i < NREG; i += 8) SPIN_DPP_FMAC8(SPIN_DPP_XOR1, r + i, s1);
+#pragma unroll
+    for (int i = 0; i < NREG; i += 8) SPIN_DPP_FMAC8(SPIN_DPP_XOR2, r + i, s2);
+#pragma unroll
+    for (int i = 0; i < NREG; i += 8) SPIN_DPP_FMAC8(SPIN_DPP_XOR7, r + i, s3);
+#pragma unroll
+    for (int i = 0; i < NREG; i += 8) SPIN_DPP_FMAC8(SPIN_DPP_XOR15, r + i, s4);
+}
+
+// Fast quantizer for a row whose scale s is in the normal range.  With
+// cr = fl32(norm / s) (signed per element as needed) the fused
+// f = fma(z, cr, kQuantMagic) lands y/s + 1/2 on a grid of 2^-16 in the low
+// mantissa bits: bits 16..19 hold the nibble of floor(y/s + 1/2) and bits
+// 0..15 the fraction, offset by one unit so that an exact tie reads 1.
+// Whenever the fraction is within one unit of a tie (bits 0..15 < 3) the
+// caller recomputes the code with the exact IEEE quotient.  The fast estimate
+// is within a few float32 ulps (< 2^-18 absolute) of fl32(y / s), so outside
+// that window both round to the same integer.
+constexpr float kQuantMagic = 192.5f + 0x1p-16f;
+
+__device__ __forceinline__ bool near_tie(uint32_t fbits) { return (fbits & 0xFFFFu) < 3u; }
+
+// Pack the nibbles held in bits 16..19 of eight magic-number results.
+__device__ __forceinline__ uint32_t pack8_magic(const uint32_t* f) {
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // byte 2 of p[i] = nib(f[2i]) | nib(f[2i+1]) << 4
+        p[i] = (f[2 * i] & 0x000F0000u) | ((f[2 * i + 1] << 4) & ~0x000F0000u);
+    const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0602u);
+    const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x0c0c0602u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+}  // namespace spin
