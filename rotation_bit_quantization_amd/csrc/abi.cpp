@@ -1,7 +1,7 @@
 // The libspin C ABI: host-side argument validation, then one launcher call.
 // Every check happens before anything is enqueued, so a rejected call writes
 // no output (declarations and contracts in include/libspin.h).
-#include "../../include/libspin.h"
+#include "libspin.h"
 
 #include <hip/hip_runtime.h>
 

@@ -97,7 +97,9 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
 //            (four DPP levels); b bits 6-7 are lane bits 4-5, b bits 8-9 the
 //            wave.
 //   LDS      the rotated values are written in natural order, 64-float rows
-//            padded to 68 so that the phase-2 reads spread over the banks.
+//            padded to 68 so that the phase-2 reads spread over the banks; the
+//            exchange runs in two rounds of six a each (26 KB of LDS per
+//            workgroup instead of 52 KB, so twice as many workgroups fit a CU).
 //   phase 2  thread holds 8 consecutive b (bits 0-2) for 6 of the 12 a: b bits
 //            6-9 are the low lane bits (four more DPP levels), b bits 3-4 lane
 //            bits 4-5, b bit 5 wave bit 0, the half of a wave bit 1.
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
 // with an exact fallback near ties, eight per dword store.
 constexpr int kLdsRowF = 68;                 // 64 floats + 4 pad
 constexpr int kLdsAF = 16 * kLdsRowF;        // one a (1024 b) = 16 padded rows
-constexpr int kLdsFloats12288 = 12 * kLdsAF;
+constexpr int kLdsFloats12288 = 6 * kLdsAF;
 
 __device__ __forceinline__ float h2f_lo(uint32_t w) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xFFFFu)));
@@ -116,9 +118,30 @@ __device__ __forceinline__ float h2f_hi(uint32_t w) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
 }
 
+// Eight magic-number results (nibble in bits 16..19) -> one dword of codes.
+__device__ __forceinline__ uint32_t pack8_magic(const uint32_t* f) {
+    // byte 2 of every result, even elements into `ev`, odd ones into `od`
+    const uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(f[6], f[4], 0x0c0c0602u),
+                                              __builtin_amdgcn_perm(f[2], f[0], 0x0c0c0602u),
+                                              0x05040100u);
+    const uint32_t od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(f[7], f[5], 0x0c0c0602u),
+                                              __builtin_amdgcn_perm(f[3], f[1], 0x0c0c0602u),
+                                              0x05040100u);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+}
+
+// True when any of eight magic-number results is within one unit of a tie.
+__device__ __forceinline__ bool any_near_tie(const uint32_t* f) {
+    const uint32_t m01 = min(f[0] & 0xFFFFu, f[1] & 0xFFFFu), m23 = min(f[2] & 0xFFFFu, f[3] & 0xFFFFu);
+    const uint32_t m45 = min(f[4] & 0xFFFFu, f[5] & 0xFFFFu), m67 = min(f[6] & 0xFFFFu, f[7] & 0xFFFFu);
+    return min(min(m01, m23), min(m45, m67)) < 3u;
+}
+
+// One row per workgroup.  `one` is 1.0f passed at run time so that
+// (x0 * one + x1) stays a mixed-precision FMA reading both fp16 halves.
 template <bool WRITE_ROT>
 __global__ __launch_bounds__(256) void fwht_quant_k12288(
-    const __half* __restrict__ X, float norm, uint8_t* __restrict__ Xq,
+    const __half* __restrict__ X, float norm, float one, uint8_t* __restrict__ Xq,
     float* __restrict__ x_scale, float* __restrict__ X_rot) {
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats12288];
     __shared__ float red[4];
@@ -127,24 +150,31 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const size_t row = blockIdx.x;
-    const __half* xr = X + row * 12288;
-
-    const float s1 = lane_sign(l16, 0b0101), s2 = lane_sign(l16, 0b0110);
-    const float s3 = lane_sign(l16, 0b1100), s4 = lane_sign(l16, 0b1000);
 
     // ---- phase 1: load x[a][4 beta .. 4 beta + 3], beta bits 0-3 permuted for DPP
     const int beta_in = g_perm(l16) | ((lane >> 4) << 4) | (wave << 6);
     uint2 raw[12];
+    {
+        const __half* xr = X + row * 12288 + 4 * beta_in;
 #pragma unroll
-    for (int a = 0; a < 12; ++a)
-        raw[a] = *reinterpret_cast<const uint2*>(xr + a * 1024 + 4 * beta_in);
+        for (int a = 0; a < 12; ++a) {  // read once: non-temporal
+            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+            const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(xr + a * 1024));
+            raw[a] = make_uint2(t.x, t.y);
+        }
+    }
+    const float s1 = lane_sign(l16, 0b0101), s2 = lane_sign(l16, 0b0110);
+    const float s3 = lane_sign(l16, 0b1100), s4 = lane_sign(l16, 0b1000);
 
+    // b bits 0-1 in registers; the first level reads both fp16 halves directly
     float v[12][4];
 #pragma unroll
     for (int a = 0; a < 12; ++a) {
-        const float x0 = h2f_lo(raw[a].x), x1 = h2f_hi(raw[a].x);
-        const float x2 = h2f_lo(raw[a].y), x3 = h2f_hi(raw[a].y);
-        const float s01 = x0 + x1, d01 = x0 - x1, s23 = x2 + x3, d23 = x2 - x3;
+        const uint32_t w0 = raw[a].x, w1 = raw[a].y;
+        const float s01 = __builtin_fmaf(h2f_lo(w0), one, h2f_hi(w0));
+        const float d01 = __builtin_fmaf(h2f_hi(w0), -one, h2f_lo(w0));
+        const float s23 = __builtin_fmaf(h2f_lo(w1), one, h2f_hi(w1));
+        const float d23 = __builtin_fmaf(h2f_hi(w1), -one, h2f_lo(w1));
         v[a][0] = s01 + s23;
         v[a][1] = d01 + d23;
         v[a][2] = s01 - s23;
@@ -161,28 +191,27 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
     }
     dpp_wht16<48>(&v[0][0], s1, s2, s3, s4);
 
-    // ---- exchange: lane i now holds natural b bits 2-5 = i
-    {
-        const int beta = l16 | ((lane >> 4) << 4) | (wave << 6);
-        float* dst = lds + (beta >> 4) * kLdsRowF + 4 * l16;
-#pragma unroll
-        for (int c = 0; c < 12; ++c)
-            *reinterpret_cast<float4*>(dst + c * kLdsAF) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
-    }
-    __syncthreads();
-
-    // ---- phase 2: 8 consecutive b of 6 rows c of the 12 x 1024 view
     const int ch = wave >> 1;
     const int blo = 8 * (((lane >> 4) & 3) | ((wave & 1) << 2));      // b & 63
     float z[6][8];
-    {
-        const float* src = lds + g_perm(l16) * kLdsRowF + blo + ch * 6 * kLdsAF;
+    const int beta = l16 | ((lane >> 4) << 4) | (wave << 6);
+    float* dst = lds + (beta >> 4) * kLdsRowF + 4 * l16;
+    const float* src = lds + g_perm(l16) * kLdsRowF + blo;
 #pragma unroll
-        for (int ci = 0; ci < 6; ++ci) {
-            const float4 p = *reinterpret_cast<const float4*>(src + ci * kLdsAF);
-            const float4 q = *reinterpret_cast<const float4*>(src + ci * kLdsAF + 4);
-            z[ci][0] = p.x; z[ci][1] = p.y; z[ci][2] = p.z; z[ci][3] = p.w;
-            z[ci][4] = q.x; z[ci][5] = q.y; z[ci][6] = q.z; z[ci][7] = q.w;
+    for (int half = 0; half < 2; ++half) {
+        if (half) __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 6; ++c)
+            *reinterpret_cast<float4*>(dst + c * kLdsAF) = make_float4(v[6*half+c][0], v[6*half+c][1], v[6*half+c][2], v[6*half+c][3]);
+        __syncthreads();
+        if (ch == half) {
+#pragma unroll
+            for (int ci = 0; ci < 6; ++ci) {
+                const float4 p = *reinterpret_cast<const float4*>(src + ci * kLdsAF);
+                const float4 q = *reinterpret_cast<const float4*>(src + ci * kLdsAF + 4);
+                z[ci][0] = p.x; z[ci][1] = p.y; z[ci][2] = p.z; z[ci][3] = p.w;
+                z[ci][4] = q.x; z[ci][5] = q.y; z[ci][6] = q.z; z[ci][7] = q.w;
+            }
         }
     }
     dpp_wht16<48>(&z[0][0], s1, s2, s3, s4);
@@ -198,29 +227,24 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
     if (tid == 0) x_scale[row] = s;
 
     // Sign of each held value relative to the true transform: phase 1 left
-    // (-1)^popcount(b2..b4), phase 2 (-1)^popcount(b6..b8) (b2 = register bit 2).
+    // (-1)^popcount(b2..b4), phase 2 (-1)^popcount(b6..b8); b2 is register bit 2.
     const int b3 = (lane >> 4) & 1, b4 = (lane >> 5) & 1;
     const bool neg_lo = ((b3 ^ b4) ^ (__builtin_popcount(l16 & 7) & 1)) != 0;
     const float sg_lo = neg_lo ? -1.0f : 1.0f;        // registers k = 0..3 (b2 = 0)
     const float sg_hi = -sg_lo;                        // registers k = 4..7 (b2 = 1)
 
-    const size_t obase = row * 6144 + (ch * 6) * 512 + (l16 * 64 + blo) / 2;
-    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + obase);
-    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
-    if (fast) {
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * 6144 + (ch * 6) * 512 + (l16 * 64 + blo) / 2);
+    if ((s >= 0x1p-100f) && (s <= 0x1p+100f)) {
         const float cr = norm * __fdiv_rn(1.0f, s);
         const float cr_lo = sg_lo * cr, cr_hi = sg_hi * cr;
 #pragma unroll
         for (int ci = 0; ci < 6; ++ci) {
             uint32_t f[8];
-            bool tie = false;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < 8; ++k)
                 f[k] = __float_as_uint(__builtin_fmaf(z[ci][k], k < 4 ? cr_lo : cr_hi, kQuantMagic));
-                tie |= near_tie(f[k]);
-            }
             uint32_t word = pack8_magic(f);
-            if (tie) {
+            if (any_near_tie(f)) {
                 int c8[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
@@ -274,10 +298,10 @@ hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h
         const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
         const __half* x = static_cast<const __half*>(X);
         if (X_rot)
-            hipLaunchKernelGGL((fwht_quant_k12288<true>), dim3(M), dim3(256), 0, s, x, norm, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288<true>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
                                x_scale, X_rot);
         else
-            hipLaunchKernelGGL((fwht_quant_k12288<false>), dim3(M), dim3(256), 0, s, x, norm, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288<false>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
                                x_scale, X_rot);
         return hipGetLastError();
     }

@@ -76,16 +76,25 @@ __device__ __forceinline__ float hadamard_sign(unsigned i, unsigned j, int log2p
     return s;
 }
 
+// Max of a float over the 16 lanes of each DPP row (every lane gets it).
+__device__ __forceinline__ float row16_max(float v) {
+    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false))); // lane ^ 7
+    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false))); // lane ^ 15
+    return v;
+}
+
 // Block-wide max of non-negative floats over 256 threads (4 waves).  `red`
 // is a __shared__ float[4]; the result is returned to every thread.
 __device__ __forceinline__ float block_max_256(float v, float* red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    v = row16_max(v);
+    v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
+    v = __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
-    float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-    return r;
+    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
 }  // namespace spin
@@ -210,16 +219,5 @@ __device__ __forceinline__ void dpp_wht16(float* r, float s1, float s2, float s3
 constexpr float kQuantMagic = 192.5f + 0x1p-16f;
 
 __device__ __forceinline__ bool near_tie(uint32_t fbits) { return (fbits & 0xFFFFu) < 3u; }
-
-// Pack the nibbles held in bits 16..19 of eight magic-number results.
-__device__ __forceinline__ uint32_t pack8_magic(const uint32_t* f) {
-    uint32_t p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)   // byte 2 of p[i] = nib(f[2i]) | nib(f[2i+1]) << 4
-        p[i] = (f[2 * i] & 0x000F0000u) | ((f[2 * i + 1] << 4) & ~0x000F0000u);
-    const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0602u);
-    const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x0c0c0602u);
-    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
 
 }  // namespace spin
