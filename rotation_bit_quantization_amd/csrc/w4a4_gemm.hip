@@ -108,19 +108,39 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
 
 // ---------------------------------------------------------------------------
 // w4a4_gemm_256: 256 x 256 output tile per workgroup of 8 waves (2 x 4), each
-// wave 128 x 64 (8 x 4 MFMA 16x16x64 tiles, int32 accumulators in the
-// accumulation registers), two waves per SIMD so that one wave's MFMAs run
-// while the other waits on LDS or widens operands.  K advances 64 codes
-// (32 bytes per row) per step; the next step's 16 KB of packed operands is
-// fetched into registers while the current step runs from LDS, then written
-// to the other half of a double-buffered LDS (2 x 16 KB): one barrier per
-// step.  Tiles are assigned so that the workgroups running on one XCD
+// wave 128 x 64 as 4 x 2 tiles of the 32x32x32 int8 MFMA (the 32x32 shape
+// sustains a higher int8 rate on gfx950 than 16x16x64), two waves per SIMD.
+//
+// Operands stream from global memory straight into LDS (global_load_lds, 16
+// bytes per lane) through a ring of kStages LDS stages of one K step each (64
+// codes = 32 bytes per row; 16 KB per stage).  Loads run kStages - 1 steps
+// ahead of the MFMAs, with one barrier per step and explicit vector-memory
+// waits (a full workgroup fence would drain every load in flight).
+//
+// LDS layout of a stage: for A then B, 8 blocks of 32 rows (1 KB each, one DMA
+// instruction of one wave); inside a block, the 16-byte slot 2 r + p holds
+// logical half h = p ^ s(r) of row r, s(r) = ((r >> 2) ^ (r >> 3)) & 1, so that
+// the 16-byte fragment reads of 8 or 16 consecutive rows at one half land in
+// distinct banks.
+//
+// MFMA 32x32x32 operand layout used here: lane l supplies row (or column)
+// l % 32 and 16 k values; lanes 0-31 take logical half 0 of the K step, lanes
+// 32-63 half 1, and the two MFMAs of a step take bytes 0-7 then 8-15 of each
+// lane's 16-byte slot (the same assignment for A and B, so the sum over the
+// 64 codes is unchanged).  Result register r of lane l holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32.
+//
+// Rows beyond M or N load row 0 instead (any valid data); their results are
+// never stored.  Tiles are assigned so that the workgroups running on one XCD
 // (hardware places workgroup i on XCD i mod 8) cover a compact block of tile
 // rows and columns, which keeps the operands they share in that XCD's L2.
 constexpr int kT = 256;
 constexpr int kStepBytes = 32;
 constexpr int kStageBytes = 2 * kT * kStepBytes;   // A then B
+constexpr int kStages = 4;
 constexpr int kGemmThreads = 512;
+
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void tile_of(int bid, int tilesM, int tilesN, int* tm, int* tn) {
     const int T = tilesM * tilesN;
@@ -135,12 +155,45 @@ __device__ __forceinline__ void tile_of(int bid, int tilesM, int tilesN, int* tm
     *tn = r / rows;
 }
 
+__device__ __forceinline__ int half_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+typedef const __attribute__((address_space(3))) void* lds_cptr;
+
+// Byte offset of a __shared__ object within the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)(p)));
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 16).
+#define SPIN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((n) | 0x0F70)
+
+// Workgroup barrier that is also a compiler memory barrier (no load or store
+// moves across it) but, unlike __syncthreads, not a memory fence: it does not
+// wait for the LDS-DMA loads still in flight for later steps.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes per lane from `src` into LDS at byte address lds_base + 16 * lane
+// (lds_base wave-uniform).  Issued from assembly so that the compiler does not
+// wait for it before unrelated LDS reads; M0 is saved and restored around it.
+// The only register operand is the address, which the load consumes at issue.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_base)
+        : "memory");
+}
+
 template <bool WRITE_ACC>
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
     const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -151,82 +204,83 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
     const size_t rowBytes = static_cast<size_t>(K) / 2;
     const int steps = K / 64;
 
-    // staging: thread t moves 16 bytes of row t / 2 of A (t < 512 covers all
-    // 256 rows) and the same of B
-    const int sr = tid >> 1, so = (tid & 1) * 16;
-    const bool oka = (m0 + sr) < M, okb = (n0 + sr) < N;
-    const uint8_t* ga = Xq + static_cast<size_t>(oka ? m0 + sr : 0) * rowBytes + so;
-    const uint8_t* gb = Wq + static_cast<size_t>(okb ? n0 + sr : 0) * rowBytes + so;
-    uint4 pa, pb;
-    auto fetch = [&](int step) {
+    // DMA source of this lane: row 32 wave + lane / 2 of A and of B, logical half
+    const int dr = lane >> 1;
+    const int dh = (lane & 1) ^ half_swz(dr);
+    const int ra = m0 + 32 * wave + dr, rb = n0 + 32 * wave + dr;
+    const uint8_t* ga = Xq + static_cast<size_t>(ra < M ? ra : 0) * rowBytes + dh * 16;
+    const uint8_t* gb = Wq + static_cast<size_t>(rb < N ? rb : 0) * rowBytes + dh * 16;
+    const uint32_t lds_wave = lds_addr(lds) + wave * 1024;
+    auto issue = [&](int step) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (step % kStages) * kStageBytes);
         const size_t off = static_cast<size_t>(step) * kStepBytes;
-        pa = oka ? *reinterpret_cast<const uint4*>(ga + off) : make_uint4(0, 0, 0, 0);
-        pb = okb ? *reinterpret_cast<const uint4*>(gb + off) : make_uint4(0, 0, 0, 0);
-    };
-    // LDS rows are 32 bytes = four 8-byte chunks; chunk c of row r is stored at
-    // slot c ^ ((r >> 2) & 3) so that the fragment reads (16 rows, same chunk)
-    // fall in distinct banks.
-    const int sw_st = (sr >> 2) & 3, c0 = (tid & 1) * 2;
-    const int st0 = sr * kStepBytes + ((c0 ^ sw_st) << 3), st1 = sr * kStepBytes + (((c0 + 1) ^ sw_st) << 3);
-    auto stash = [&](int buf) {
-        uint8_t* base = lds + buf * kStageBytes;
-        *reinterpret_cast<uint2*>(base + st0) = make_uint2(pa.x, pa.y);
-        *reinterpret_cast<uint2*>(base + st1) = make_uint2(pa.z, pa.w);
-        *reinterpret_cast<uint2*>(base + kT * kStepBytes + st0) = make_uint2(pb.x, pb.y);
-        *reinterpret_cast<uint2*>(base + kT * kStepBytes + st1) = make_uint2(pb.z, pb.w);
+        lds_dma16(ga + off, base);
+        lds_dma16(gb + off, base + kT * kStepBytes);
     };
 
-    v4i acc[8][4];
+    v16i acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    const int fr = lane & 15, fk = ((lane >> 4) ^ ((fr >> 2) & 3)) * 8;   // swizzled chunk
+    // fragment reads: row l % 32 of a 32-row block, logical half l / 32
+    const int fr = lane & 31;
+    const int fo = fr * kStepBytes + (((lane >> 5) ^ half_swz(fr)) << 4);
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < steps) issue(s);
+
     for (int step = 0; step < steps; ++step) {
-        const int buf = step & 1;
-        if (step + 1 < steps) fetch(step + 1);
-        const uint8_t* sa = lds + buf * kStageBytes + (wm + fr) * kStepBytes + fk;
-        const uint8_t* sb = lds + buf * kStageBytes + kT * kStepBytes + (wn + fr) * kStepBytes + fk;
-        v4i fb[4];
+        // This wave's loads of `step` are done once at most (later steps in
+        // flight) x 2 remain; the barrier then also guarantees that every
+        // wave has finished reading the stage refilled below.
+        const int later = min(kStages - 2, steps - 1 - step);
+        if (later >= 2) SPIN_WAIT_VMCNT(4);
+        else if (later == 1) SPIN_WAIT_VMCNT(2);
+        else SPIN_WAIT_VMCNT(0);
+        barrier_no_fence();
+        if (step + kStages - 1 < steps) issue(step + kStages - 1);
+        const uint8_t* st = lds + (step % kStages) * kStageBytes;
+        const uint8_t* sa = st + wm * kStepBytes + fo;
+        const uint8_t* sb = st + kT * kStepBytes + wn * kStepBytes + fo;
+        uint4 qb[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = widen16(*reinterpret_cast<const uint2*>(sb + j * 16 * kStepBytes));
+        for (int j = 0; j < 2; ++j) qb[j] = *reinterpret_cast<const uint4*>(sb + j * 32 * kStepBytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const v4i fa = widen16(*reinterpret_cast<const uint2*>(sa + i * 16 * kStepBytes));
+        for (int i = 0; i < 4; ++i) {
+            const uint4 qa = *reinterpret_cast<const uint4*>(sa + i * 32 * kStepBytes);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa, fb[j], acc[i][j], 0, 0, 0);
+            for (int sub = 0; sub < 2; ++sub) {
+                const v4i fa = widen16(sub ? make_uint2(qa.z, qa.w) : make_uint2(qa.x, qa.y));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const v4i fb = widen16(sub ? make_uint2(qb[j].z, qb[j].w) : make_uint2(qb[j].x, qb[j].y));
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb, acc[i][j], 0, 0, 0);
+                }
+            }
         }
-        if (step + 1 < steps) stash(buf ^ 1);
-        __syncthreads();
     }
 
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float sx[4];
-        int rows[4];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            rows[r] = m0 + wm + i * 16 + (lane >> 4) * 4 + r;
-            sx[r] = rows[r] < M ? x_scale[rows[r]] : 0.0f;
-        }
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row >= M) continue;
+            const float sx = x_scale[row];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn + j * 16 + (lane & 15);
-            if (col >= N) continue;
-            const float sw = w_scale[col];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (rows[r] < M) {
+            for (int j = 0; j < 2; ++j) {
+                const int col = n0 + wn + j * 32 + (lane & 31);
+                if (col < N) {
                     const int a = acc[i][j][r] >> 8;
-                    float y = static_cast<float>(a) * sx[r];
-                    y = y * sw;
-                    Y[static_cast<size_t>(rows[r]) * N + col] = y;
-                    if (WRITE_ACC) acc_out[static_cast<size_t>(rows[r]) * N + col] = a;
+                    float y = static_cast<float>(a) * sx;
+                    y = y * w_scale[col];
+                    Y[static_cast<size_t>(row) * N + col] = y;
+                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                 }
             }
         }
