@@ -112,33 +112,37 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
 // sustains a higher int8 rate on gfx950 than 16x16x64), two waves per SIMD.
 //
 // Operands stream from global memory straight into LDS (global_load_lds, 16
-// bytes per lane) through a ring of kStages LDS stages of one K step each (64
-// codes = 32 bytes per row; 16 KB per stage).  Loads run kStages - 1 steps
-// ahead of the MFMAs, with one barrier per step and explicit vector-memory
-// waits (a full workgroup fence would drain every load in flight).
+// bytes per lane) through a ring of kStages LDS stages of one K step each
+// (128 codes = 64 bytes per row; 32 KB per stage).  Loads run kStages - 1
+// steps ahead of the MFMAs, with one barrier per step and explicit
+// vector-memory waits (a full workgroup fence would drain every load in
+// flight).  These loads are issued from assembly: the compiler would
+// otherwise wait for all of them before every LDS read.
 //
-// LDS layout of a stage: for A then B, 8 blocks of 32 rows (1 KB each, one DMA
-// instruction of one wave); inside a block, the 16-byte slot 2 r + p holds
-// logical half h = p ^ s(r) of row r, s(r) = ((r >> 2) ^ (r >> 3)) & 1, so that
-// the 16-byte fragment reads of 8 or 16 consecutive rows at one half land in
+// LDS layout of a stage: for A then B, 8 blocks of 32 rows (2 KB each, two DMA
+// instructions of one wave); inside a block the 16-byte slot 4 r + p holds
+// logical slot h = p ^ f(r) of row r, f(r) = ((r >> 1) ^ (r >> 3)) & 3, so that
+// 16-byte reads of one logical slot by 8 (or 16) consecutive rows touch
 // distinct banks.
 //
 // MFMA 32x32x32 operand layout used here: lane l supplies row (or column)
-// l % 32 and 16 k values; lanes 0-31 take logical half 0 of the K step, lanes
-// 32-63 half 1, and the two MFMAs of a step take bytes 0-7 then 8-15 of each
-// lane's 16-byte slot (the same assignment for A and B, so the sum over the
-// 64 codes is unchanged).  Result register r of lane l holds row
-// 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32.
+// l % 32 and 16 k values; lanes 0-31 take logical slots 0-1 of the step,
+// lanes 32-63 slots 2-3, and the four MFMAs of a step take bytes 0-7 and 8-15
+// of the lane's first slot, then of its second (the same assignment for A
+// and B, so the sum over the 128 codes is unchanged).  Result register r of
+// lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32.
 //
 // Rows beyond M or N load row 0 instead (any valid data); their results are
 // never stored.  Tiles are assigned so that the workgroups running on one XCD
 // (hardware places workgroup i on XCD i mod 8) cover a compact block of tile
 // rows and columns, which keeps the operands they share in that XCD's L2.
 constexpr int kT = 256;
-constexpr int kStepBytes = 32;
+constexpr int kStepCodes = 128;
+constexpr int kStepBytes = kStepCodes / 2;
 constexpr int kStageBytes = 2 * kT * kStepBytes;   // A then B
 constexpr int kStages = 4;
 constexpr int kGemmThreads = 512;
+constexpr int kGemmMinK = kStepCodes;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -155,7 +159,7 @@ __device__ __forceinline__ void tile_of(int bid, int tilesM, int tilesN, int* tm
     *tn = r / rows;
 }
 
-__device__ __forceinline__ int half_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__device__ __forceinline__ int slot_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 typedef const __attribute__((address_space(3))) void* lds_cptr;
 
@@ -173,9 +177,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // 16 bytes per lane from `src` into LDS at byte address lds_base + 16 * lane
-// (lds_base wave-uniform).  Issued from assembly so that the compiler does not
-// wait for it before unrelated LDS reads; M0 is saved and restored around it.
-// The only register operand is the address, which the load consumes at issue.
+// (lds_base wave-uniform).  M0 is saved and restored around it; the only
+// register operand is the address, which the load consumes at issue.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
@@ -202,20 +205,29 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
     const int m0 = tm * kT, n0 = tn * kT;
     const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
     const size_t rowBytes = static_cast<size_t>(K) / 2;
-    const int steps = K / 64;
+    const int steps = K / kStepCodes;
 
-    // DMA source of this lane: row 32 wave + lane / 2 of A and of B, logical half
-    const int dr = lane >> 1;
-    const int dh = (lane & 1) ^ half_swz(dr);
-    const int ra = m0 + 32 * wave + dr, rb = n0 + 32 * wave + dr;
-    const uint8_t* ga = Xq + static_cast<size_t>(ra < M ? ra : 0) * rowBytes + dh * 16;
-    const uint8_t* gb = Wq + static_cast<size_t>(rb < N ? rb : 0) * rowBytes + dh * 16;
-    const uint32_t lds_wave = lds_addr(lds) + wave * 1024;
+    // DMA sources of this lane (two instructions per operand): 16-byte slot
+    // q = 64 d + lane of the wave's 2 KB block = row q / 4, physical slot q % 4
+    const uint8_t* ga[2];
+    const uint8_t* gb[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const int q = 64 * d + lane;
+        const int r = q >> 2;
+        const int h = (q & 3) ^ slot_swz(r);
+        const int ra = m0 + 32 * wave + r, rb = n0 + 32 * wave + r;
+        ga[d] = Xq + static_cast<size_t>(ra < M ? ra : 0) * rowBytes + h * 16;
+        gb[d] = Wq + static_cast<size_t>(rb < N ? rb : 0) * rowBytes + h * 16;
+    }
+    const uint32_t lds_wave = lds_addr(lds) + wave * 2048;
     auto issue = [&](int step) {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (step % kStages) * kStageBytes);
         const size_t off = static_cast<size_t>(step) * kStepBytes;
-        lds_dma16(ga + off, base);
-        lds_dma16(gb + off, base + kT * kStepBytes);
+        lds_dma16(ga[0] + off, base);
+        lds_dma16(ga[1] + off, base + 1024);
+        lds_dma16(gb[0] + off, base + kT * kStepBytes);
+        lds_dma16(gb[1] + off, base + kT * kStepBytes + 1024);
     };
 
     v16i acc[4][2];
@@ -226,9 +238,12 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // fragment reads: row l % 32 of a 32-row block, logical half l / 32
+    // fragment reads: row l % 32 of a 32-row block, logical slots 2 (l / 32)
+    // and 2 (l / 32) + 1
     const int fr = lane & 31;
-    const int fo = fr * kStepBytes + (((lane >> 5) ^ half_swz(fr)) << 4);
+    const int h0 = 2 * (lane >> 5);
+    const int fo0 = fr * kStepBytes + ((h0 ^ slot_swz(fr)) << 4);
+    const int fo1 = fr * kStepBytes + (((h0 + 1) ^ slot_swz(fr)) << 4);
 
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
@@ -236,30 +251,34 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 
     for (int step = 0; step < steps; ++step) {
         // This wave's loads of `step` are done once at most (later steps in
-        // flight) x 2 remain; the barrier then also guarantees that every
+        // flight) x 4 remain; the barrier then also guarantees that every
         // wave has finished reading the stage refilled below.
         const int later = min(kStages - 2, steps - 1 - step);
-        if (later >= 2) SPIN_WAIT_VMCNT(4);
-        else if (later == 1) SPIN_WAIT_VMCNT(2);
+        if (later >= 2) SPIN_WAIT_VMCNT(8);
+        else if (later == 1) SPIN_WAIT_VMCNT(4);
         else SPIN_WAIT_VMCNT(0);
         barrier_no_fence();
         if (step + kStages - 1 < steps) issue(step + kStages - 1);
         const uint8_t* st = lds + (step % kStages) * kStageBytes;
-        const uint8_t* sa = st + wm * kStepBytes + fo;
-        const uint8_t* sb = st + kT * kStepBytes + wn * kStepBytes + fo;
-        uint4 qb[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) qb[j] = *reinterpret_cast<const uint4*>(sb + j * 32 * kStepBytes);
+        for (int part = 0; part < 2; ++part) {
+            const int fo = part ? fo1 : fo0;
+            const uint8_t* sa = st + wm * kStepBytes + fo;
+            const uint8_t* sb = st + kT * kStepBytes + wn * kStepBytes + fo;
+            uint4 qb[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 qa = *reinterpret_cast<const uint4*>(sa + i * 32 * kStepBytes);
+            for (int j = 0; j < 2; ++j) qb[j] = *reinterpret_cast<const uint4*>(sb + j * 32 * kStepBytes);
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const v4i fa = widen16(sub ? make_uint2(qa.z, qa.w) : make_uint2(qa.x, qa.y));
+            for (int i = 0; i < 4; ++i) {
+                const uint4 qa = *reinterpret_cast<const uint4*>(sa + i * 32 * kStepBytes);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const v4i fb = widen16(sub ? make_uint2(qb[j].z, qb[j].w) : make_uint2(qb[j].x, qb[j].y));
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb, acc[i][j], 0, 0, 0);
+                for (int sub = 0; sub < 2; ++sub) {
+                    const v4i fa = widen16(sub ? make_uint2(qa.z, qa.w) : make_uint2(qa.x, qa.y));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const v4i fb = widen16(sub ? make_uint2(qb[j].z, qb[j].w) : make_uint2(qb[j].x, qb[j].y));
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb, acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -292,13 +311,25 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, hipStream_t s) {
-    const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
+    if (K % kStepCodes == 0) {
+        const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
+        dim3 grid(static_cast<unsigned>(tiles));
+        if (acc_out)
+            hipLaunchKernelGGL((w4a4_gemm_256<true>), grid, dim3(kGemmThreads), 0, s, Xq, x_scale,
+                               Wq, w_scale, M, N, K, Y, acc_out);
+        else
+            hipLaunchKernelGGL((w4a4_gemm_256<false>), grid, dim3(kGemmThreads), 0, s, Xq, x_scale,
+                               Wq, w_scale, M, N, K, Y, acc_out);
+        return hipGetLastError();
+    }
+    // K a multiple of 64 but not of 128: 128 x 128 tiles, 64-code steps
+    const long long tiles = static_cast<long long>((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
     dim3 grid(static_cast<unsigned>(tiles));
     if (acc_out)
-        hipLaunchKernelGGL((w4a4_gemm_256<true>), grid, dim3(kGemmThreads), 0, s, Xq, x_scale, Wq,
+        hipLaunchKernelGGL((w4a4_gemm_basic<true>), grid, dim3(256), 0, s, Xq, x_scale, Wq,
                            w_scale, M, N, K, Y, acc_out);
     else
-        hipLaunchKernelGGL((w4a4_gemm_256<false>), grid, dim3(kGemmThreads), 0, s, Xq, x_scale, Wq,
+        hipLaunchKernelGGL((w4a4_gemm_basic<false>), grid, dim3(256), 0, s, Xq, x_scale, Wq,
                            w_scale, M, N, K, Y, acc_out);
     return hipGetLastError();
 }
