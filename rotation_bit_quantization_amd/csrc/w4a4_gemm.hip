@@ -107,9 +107,10 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
 }
 
 // ---------------------------------------------------------------------------
-// w4a4_gemm_256: 256 x 256 output tile per workgroup of 8 waves (2 x 4), each
-// wave 128 x 64 as 4 x 2 tiles of the 32x32x32 int8 MFMA (the 32x32 shape
-// sustains a higher int8 rate on gfx950 than 16x16x64), two waves per SIMD.
+// w4a4_gemm_256: 256 x 256 output tile per workgroup of 16 waves (4 x 4), each
+// wave 64 x 64 as 2 x 2 tiles of the 32x32x32 int8 MFMA (the 32x32 shape
+// sustains a higher int8 rate on gfx950 than 16x16x64), four waves per SIMD so
+// that LDS latency and the per-step barrier are hidden behind other waves.
 //
 // Operands stream from global memory straight into LDS (global_load_lds, 16
 // bytes per lane) through a ring of kStages LDS stages of one K step each
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
 // flight).  These loads are issued from assembly: the compiler would
 // otherwise wait for all of them before every LDS read.
 //
-// LDS layout of a stage: for A then B, 8 blocks of 32 rows (2 KB each, two DMA
-// instructions of one wave); inside a block the 16-byte slot 4 r + p holds
+// LDS layout of a stage: for A then B, 8 blocks of 32 rows (2 KB each, one DMA
+// instruction from each of two waves); inside a block the 16-byte slot 4 r + p holds
 // logical slot h = p ^ f(r) of row r, f(r) = ((r >> 1) ^ (r >> 3)) & 3, so that
 // 16-byte reads of one logical slot by 8 (or 16) consecutive rows touch
 // distinct banks.
@@ -141,7 +142,7 @@ constexpr int kStepCodes = 128;
 constexpr int kStepBytes = kStepCodes / 2;
 constexpr int kStageBytes = 2 * kT * kStepBytes;   // A then B
 constexpr int kStages = 4;
-constexpr int kGemmThreads = 512;
+constexpr int kGemmThreads = 1024;
 constexpr int kGemmMinK = kStepCodes;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -203,36 +204,34 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
     int tm, tn;
     tile_of(blockIdx.x, (M + kT - 1) / kT, (N + kT - 1) / kT, &tm, &tn);
     const int m0 = tm * kT, n0 = tn * kT;
-    const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+    const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
     const size_t rowBytes = static_cast<size_t>(K) / 2;
     const int steps = K / kStepCodes;
 
-    // DMA sources of this lane (two instructions per operand): 16-byte slot
-    // q = 64 d + lane of the wave's 2 KB block = row q / 4, physical slot q % 4
-    const uint8_t* ga[2];
-    const uint8_t* gb[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        const int q = 64 * d + lane;
+    // DMA source of this lane: the wave fills rows 16 (wave & 1) .. + 15 of the
+    // 32-row block wave / 2; 16-byte slot q = 64 (wave & 1) + lane of the block
+    // = row q / 4, physical slot q % 4
+    const uint8_t* ga;
+    const uint8_t* gb;
+    {
+        const int q = 64 * (wave & 1) + lane;
         const int r = q >> 2;
         const int h = (q & 3) ^ slot_swz(r);
-        const int ra = m0 + 32 * wave + r, rb = n0 + 32 * wave + r;
-        ga[d] = Xq + static_cast<size_t>(ra < M ? ra : 0) * rowBytes + h * 16;
-        gb[d] = Wq + static_cast<size_t>(rb < N ? rb : 0) * rowBytes + h * 16;
+        const int ra = m0 + 32 * (wave >> 1) + r, rb = n0 + 32 * (wave >> 1) + r;
+        ga = Xq + static_cast<size_t>(ra < M ? ra : 0) * rowBytes + h * 16;
+        gb = Wq + static_cast<size_t>(rb < N ? rb : 0) * rowBytes + h * 16;
     }
-    const uint32_t lds_wave = lds_addr(lds) + wave * 2048;
+    const uint32_t lds_wave = lds_addr(lds) + wave * 1024;
     auto issue = [&](int step) {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (step % kStages) * kStageBytes);
         const size_t off = static_cast<size_t>(step) * kStepBytes;
-        lds_dma16(ga[0] + off, base);
-        lds_dma16(ga[1] + off, base + 1024);
-        lds_dma16(gb[0] + off, base + kT * kStepBytes);
-        lds_dma16(gb[1] + off, base + kT * kStepBytes + 1024);
+        lds_dma16(ga + off, base);
+        lds_dma16(gb + off, base + kT * kStepBytes);
     };
 
-    v16i acc[4][2];
+    v16i acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -254,38 +253,46 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
         // flight) x 4 remain; the barrier then also guarantees that every
         // wave has finished reading the stage refilled below.
         const int later = min(kStages - 2, steps - 1 - step);
-        if (later >= 2) SPIN_WAIT_VMCNT(8);
-        else if (later == 1) SPIN_WAIT_VMCNT(4);
+        if (later >= 2) SPIN_WAIT_VMCNT(4);
+        else if (later == 1) SPIN_WAIT_VMCNT(2);
         else SPIN_WAIT_VMCNT(0);
         barrier_no_fence();
         if (step + kStages - 1 < steps) issue(step + kStages - 1);
         const uint8_t* st = lds + (step % kStages) * kStageBytes;
+        // all fragments of the step first, then the MFMAs ordered so that
+        // consecutive ones never update the same accumulator
+        uint4 qa[2][2], qb[2][2];
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
             const int fo = part ? fo1 : fo0;
-            const uint8_t* sa = st + wm * kStepBytes + fo;
-            const uint8_t* sb = st + kT * kStepBytes + wn * kStepBytes + fo;
-            uint4 qb[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) qb[j] = *reinterpret_cast<const uint4*>(sb + j * 32 * kStepBytes);
+            for (int j = 0; j < 2; ++j)
+                qb[part][j] = *reinterpret_cast<const uint4*>(st + kT * kStepBytes + (wn + j * 32) * kStepBytes + fo);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 qa = *reinterpret_cast<const uint4*>(sa + i * 32 * kStepBytes);
+            for (int i = 0; i < 2; ++i)
+                qa[part][i] = *reinterpret_cast<const uint4*>(st + (wm + i * 32) * kStepBytes + fo);
+        }
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    const v4i fa = widen16(sub ? make_uint2(qa.z, qa.w) : make_uint2(qa.x, qa.y));
+        for (int ks = 0; ks < 4; ++ks) {
+            const int part = ks >> 1, sub = ks & 1;
+            v4i fb[2];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const v4i fb = widen16(sub ? make_uint2(qb[j].z, qb[j].w) : make_uint2(qb[j].x, qb[j].y));
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb, acc[i][j], 0, 0, 0);
-                    }
-                }
+            for (int j = 0; j < 2; ++j)
+                fb[j] = widen16(sub ? make_uint2(qb[part][j].z, qb[part][j].w)
+                                    : make_uint2(qb[part][j].x, qb[part][j].y));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v4i fa = widen16(sub ? make_uint2(qa[part][i].z, qa[part][i].w)
+                                           : make_uint2(qa[part][i].x, qa[part][i].y));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[j], acc[i][j], 0, 0, 0);
             }
         }
     }
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
