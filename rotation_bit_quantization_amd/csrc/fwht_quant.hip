@@ -276,6 +276,101 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
     }
 }
 
+// ---------------------------------------------------------------------------
+// quant_rows: had_n = 1 (the rows are already in the rotated basis, e.g. R1
+// folded upstream): per-token INT4 only.  One workgroup of 256 threads per
+// row; thread t holds the chunks of 8 consecutive values t, t + 256, ...
+// (NCH of them, one 16-byte fp16 load each), so the row never leaves
+// registers: block absmax, then the magic-number quantizer with its exact
+// fallback near ties, one dword of codes per chunk.
+template <typename TIn>
+__device__ __forceinline__ void load_chunk8(const TIn* p, float* v);
+template <>
+__device__ __forceinline__ void load_chunk8<__half>(const __half* p, float* v) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    v[0] = h2f_lo(raw.x); v[1] = h2f_hi(raw.x); v[2] = h2f_lo(raw.y); v[3] = h2f_hi(raw.y);
+    v[4] = h2f_lo(raw.z); v[5] = h2f_hi(raw.z); v[6] = h2f_lo(raw.w); v[7] = h2f_hi(raw.w);
+}
+template <>
+__device__ __forceinline__ void load_chunk8<float>(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename TIn, int NCH, bool WRITE_ROT>
+__global__ __launch_bounds__(256) void quant_rows(const TIn* __restrict__ X, int K,
+                                                  uint8_t* __restrict__ Xq,
+                                                  float* __restrict__ x_scale,
+                                                  float* __restrict__ X_rot) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const size_t row = blockIdx.x;
+    const int nch = K / 8;
+    float v[NCH][8];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c < nch) {
+            load_chunk8<TIn>(X + row * K + 8 * c, v[i]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[i][k] = 0.0f;
+        }
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[i][k]));
+    const float s = __fdiv_rn(block_max_256(mx, red), kSeven);
+    if (tid == 0) x_scale[row] = s;
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * (K / 2));
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    const float cr = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c >= nch) break;
+        uint32_t word;
+        bool exact = !fast;
+        if (fast) {
+            uint32_t f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(v[i][k], cr, kQuantMagic));
+            word = pack8_magic(f);
+            exact = any_near_tie(f);
+        }
+        if (exact) {
+            int c8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c8[k] = quant_exact(v[i][k], s);
+            word = pack8(c8);
+        }
+        out[c] = word;
+        if (WRITE_ROT) {
+            float4* yr = reinterpret_cast<float4*>(X_rot + row * K + 8 * c);
+            yr[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+            yr[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+        }
+    }
+}
+
+template <typename TIn, bool WR>
+hipError_t launch_quant_rows(const TIn* X, int M, int K, uint8_t* Xq, float* xs, float* Xr,
+                             hipStream_t s) {
+    const int nch = K / 8;
+    if (nch <= 256)
+        hipLaunchKernelGGL((quant_rows<TIn, 1, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+    else if (nch <= 512)
+        hipLaunchKernelGGL((quant_rows<TIn, 2, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+    else if (nch <= 1024)
+        hipLaunchKernelGGL((quant_rows<TIn, 4, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+    else
+        hipLaunchKernelGGL((quant_rows<TIn, 8, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+    return hipGetLastError();
+}
+
 template <typename TIn, bool WR>
 hipError_t launch_rowlds(const TIn* X, int M, int K, HadOrder h, uint8_t* Xq, float* xs,
                          float* Xr, hipStream_t s) {
@@ -304,6 +399,16 @@ hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h
             hipLaunchKernelGGL((fwht_quant_k12288<false>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
                                x_scale, X_rot);
         return hipGetLastError();
+    }
+    if (h.n == 1 && K <= 16384) {
+        if (x_f16) {
+            const __half* x = static_cast<const __half*>(X);
+            return X_rot ? launch_quant_rows<__half, true>(x, M, K, Xq, x_scale, X_rot, s)
+                         : launch_quant_rows<__half, false>(x, M, K, Xq, x_scale, X_rot, s);
+        }
+        const float* x = static_cast<const float*>(X);
+        return X_rot ? launch_quant_rows<float, true>(x, M, K, Xq, x_scale, X_rot, s)
+                     : launch_quant_rows<float, false>(x, M, K, Xq, x_scale, X_rot, s);
     }
     if (x_f16) {
         const __half* x = static_cast<const __half*>(X);

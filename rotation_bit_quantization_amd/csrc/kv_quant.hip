@@ -6,9 +6,11 @@
 // Layout: one (token, head) vector of 128 values is owned by 16 lanes, 8
 // consecutive values each (a 16-byte fp16 load per lane, fully coalesced).
 // The three low index bits are butterflied in registers, the four high bits
-// across the 16 lanes of a DPP row; the absmax is reduced across the same 16
-// lanes.  Each lane then writes one dword of 8 packed codes, so a vector's 64
-// code bytes are one contiguous 64-byte store.
+// across the 16 lanes of a DPP row (fused v_fmac_f32_dpp); the absmax is
+// reduced across the same 16 lanes with DPP.  Each lane then writes one dword
+// of 8 packed codes, so a vector's 64 code bytes are one contiguous 64-byte
+// store.  The normalisation 1/sqrt(128) is applied only where values are
+// written or quantized (folded into the quantizer constant).
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -40,62 +42,127 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Quantize eight held values z (true value = sign * z * norm) of one vector
+// whose fp16 scale is s16: returns one dword of codes.  Fast path when s16 is
+// a normal fp16 (then |y / s16| < 7.5 so no clamp is needed and the
+// magic-number estimate plus exact near-tie fallback applies); otherwise the
+// exact quotient and clamp.
+__device__ __forceinline__ uint32_t kv_codes(const float* z, float sign, float norm, float sf) {
+    if (sf >= 0x1p-14f && sf <= 65504.0f) {
+        const float cr = sign * (norm * __fdiv_rn(1.0f, sf));
+        uint32_t f[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], cr, kQuantMagic));
+        const uint32_t m01 = min(f[0] & 0xFFFFu, f[1] & 0xFFFFu), m23 = min(f[2] & 0xFFFFu, f[3] & 0xFFFFu);
+        const uint32_t m45 = min(f[4] & 0xFFFFu, f[5] & 0xFFFFu), m67 = min(f[6] & 0xFFFFu, f[7] & 0xFFFFu);
+        if (min(min(m01, m23), min(m45, m67)) >= 3u) {
+            const uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(f[6], f[4], 0x0c0c0602u),
+                                                      __builtin_amdgcn_perm(f[2], f[0], 0x0c0c0602u), 0x05040100u);
+            const uint32_t od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(f[7], f[5], 0x0c0c0602u),
+                                                      __builtin_amdgcn_perm(f[3], f[1], 0x0c0c0602u), 0x05040100u);
+            return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+        }
+    }
+    int c8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c8[k] = quant_exact((z[k] * sign) * norm, sf);
+    return pack8(c8);
+}
+
+// Two (token, head) vectors per 16-lane group: lane l holds values
+// 8 g(l) .. 8 g(l) + 7 of each, g the DPP-basis load permutation, so that the
+// four cross-lane butterfly levels (one v_fmac_f32_dpp each) leave lane l with
+// values 8 l .. 8 l + 7 of the transform times (-1)^popcount(l & 7).  The
+// first in-register level reads both fp16 halves with a mixed-precision FMA
+// (`one` = 1.0 passed at run time keeps it an FMA).
 template <typename TIn, bool ROTATE, bool QUANT, bool WRITE_ROT>
 __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
-    const TIn* __restrict__ X, long long groups, float norm, uint8_t* __restrict__ codes,
+    const TIn* __restrict__ X, long long groups, float norm, float one, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scale, float* __restrict__ X_rot) {
-    const long long g = static_cast<long long>(blockIdx.x) * kKvGroupsPerBlock + (threadIdx.x >> 4);
+    constexpr int kPer = 2;
     const int l = threadIdx.x & 15;
-    if (g >= groups) return;  // the 16 lanes of a vector leave together
+    const long long g0 = (static_cast<long long>(blockIdx.x) * kKvGroupsPerBlock + (threadIdx.x >> 4)) * kPer;
+    if (g0 >= groups) return;  // the 16 lanes of a group leave together
+    const int src = ROTATE ? g_perm(l) : l;
 
-    float v[8];
-    load8<TIn>(X + g * 128 + l * 8, v);
-
+    float v[kPer][8];
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        const long long g = g0 + p < groups ? g0 + p : g0;
+        if (sizeof(TIn) == 2) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(X + g * 128 + src * 8);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            if (ROTATE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // level over index bit 0, straight from fp16
+                    const float lo = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xFFFFu)));
+                    const float hi = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+                    v[p][2 * i] = __builtin_fmaf(lo, one, hi);
+                    v[p][2 * i + 1] = __builtin_fmaf(hi, -one, lo);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[p][2 * i] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xFFFFu)));
+                    v[p][2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+                }
+            }
+        } else {
+            load8<TIn>(X + g * 128 + src * 8, v[p]);
+            if (ROTATE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = v[p][2 * i], b = v[p][2 * i + 1];
+                    v[p][2 * i] = a + b;
+                    v[p][2 * i + 1] = a - b;
+                }
+            }
+        }
+    }
+    float sign = 1.0f;
     if (ROTATE) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] *= norm;
+        for (int p = 0; p < kPer; ++p) {
 #pragma unroll
-        for (int h = 1; h < 8; h <<= 1) {
+            for (int h = 2; h < 8; h <<= 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j & h) continue;
-                const float a = v[j];
-                const float b = v[j + h];
-                v[j] = a + b;
-                v[j + h] = a - b;
+                for (int j = 0; j < 8; ++j) {
+                    if (j & h) continue;
+                    const float a = v[p][j];
+                    const float b = v[p][j + h];
+                    v[p][j] = a + b;
+                    v[p][j + h] = a - b;
+                }
             }
         }
+        dpp_wht16<16>(&v[0][0], lane_sign(l, 0b0101), lane_sign(l, 0b0110), lane_sign(l, 0b1100),
+                      lane_sign(l, 0b1000));
+        sign = lane_sign(l, 0b0111);
+    }
+    const float nrm = ROTATE ? norm : 1.0f;
+
 #pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) {
-            const bool upper = (l & msk) != 0;
+    for (int p = 0; p < kPer; ++p) {
+        const long long g = g0 + p;
+        if (g >= groups) break;
+        if (WRITE_ROT) {
+            float y[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = __shfl_xor(v[j], msk, 16);
-                v[j] = upper ? (p - v[j]) : (v[j] + p);
-            }
+            for (int k = 0; k < 8; ++k) y[k] = (v[p][k] * sign) * nrm;
+            float4* out = reinterpret_cast<float4*>(X_rot + g * 128 + l * 8);
+            out[0] = make_float4(y[0], y[1], y[2], y[3]);
+            out[1] = make_float4(y[4], y[5], y[6], y[7]);
         }
-    }
-
-    if (WRITE_ROT) {
-        float4* out = reinterpret_cast<float4*>(X_rot + g * 128 + l * 8);
-        out[0] = make_float4(v[0], v[1], v[2], v[3]);
-        out[1] = make_float4(v[4], v[5], v[6], v[7]);
-    }
-
-    if (QUANT) {
-        float mx = 0.0f;
+        if (QUANT) {
+            float mx = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[j]));
-#pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, msk, 16));
-        const float s32 = __fdiv_rn(mx, kSeven);
-        const __half s16 = __float2half_rn(s32);
-        const float sf = __half2float(s16);
-        int c8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) c8[j] = quant_exact(v[j], sf);
-        reinterpret_cast<uint32_t*>(codes)[g * 16 + l] = pack8(c8);
-        if (l == 0) scale[g] = __half_as_ushort(s16);
+            for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[p][k]));
+            mx = row16_max(mx) * nrm;                 // = max_i fl32(|z_i| * norm)
+            const __half s16 = __float2half_rn(__fdiv_rn(mx, kSeven));
+            const float sf = __half2float(s16);
+            reinterpret_cast<uint32_t*>(codes)[g * 16 + l] = kv_codes(v[p], sign, nrm, sf);
+            if (l == 0) scale[g] = __half_as_ushort(s16);
+        }
     }
 }
 
@@ -103,9 +170,10 @@ template <typename TIn, bool ROTATE, bool QUANT, bool WR>
 hipError_t launch_kv_t(const TIn* X, long long groups, uint8_t* codes, uint16_t* scale,
                        float* Xr, hipStream_t s) {
     const float norm = static_cast<float>(1.0 / __builtin_sqrt(128.0));
-    const long long blocks = (groups + kKvGroupsPerBlock - 1) / kKvGroupsPerBlock;
+    const long long per_block = 2LL * kKvGroupsPerBlock;
+    const long long blocks = (groups + per_block - 1) / per_block;
     hipLaunchKernelGGL((kv_quant_kernel<TIn, ROTATE, QUANT, WR>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kKvThreads), 0, s, X, groups, norm, codes, scale, Xr);
+                       dim3(kKvThreads), 0, s, X, groups, norm, 1.0f, codes, scale, Xr);
     return hipGetLastError();
 }
 

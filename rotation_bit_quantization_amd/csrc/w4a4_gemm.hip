@@ -313,11 +313,80 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
     }
 }
 
+// ---------------------------------------------------------------------------
+// w4a4_gemm_m16: decode-sized M <= 16, where the product is bound by reading
+// the weights once.  One workgroup per 16 output columns; its 8 waves split K
+// into 8 ranges of 128-code chunks, each wave runs two 16x16x64 int8 MFMA
+// chains over its range (lane l: row / column l % 16, 16 bytes at offset
+// 16 (l / 16) of each 64-byte chunk, the MFMA pair taking bytes 0-7 then
+// 8-15, identically for both operands), and the eight partial accumulators
+// are added exactly in LDS.  Rows beyond M and columns beyond N read row 0 /
+// the last column (valid memory) and are never stored.
+constexpr int kDecodeWaves = 8;
+
+template <bool WRITE_ACC>
+__global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    __shared__ v4i part[kDecodeWaves][64];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n0 = blockIdx.x * 16;
+    const int ra = min(lane & 15, M - 1);
+    const int cb = min(n0 + (lane & 15), N - 1);
+    const size_t rowBytes = static_cast<size_t>(K) / 2;
+    const uint8_t* pa = Xq + static_cast<size_t>(ra) * rowBytes + 16 * (lane >> 4);
+    const uint8_t* pb = Wq + static_cast<size_t>(cb) * rowBytes + 16 * (lane >> 4);
+    const int chunks = K / 128;
+    const int beg = (chunks * wave) / kDecodeWaves, end = (chunks * (wave + 1)) / kDecodeWaves;
+    v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+#pragma unroll 4
+    for (int it = beg; it < end; ++it) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(pa + static_cast<size_t>(it) * 64);
+        const uint4 qb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(it) * 64);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.x, qa.y)),
+                                                     widen16(make_uint2(qb.x, qb.y)), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.z, qa.w)),
+                                                     widen16(make_uint2(qb.z, qb.w)), acc1, 0, 0, 0);
+    }
+    part[wave][lane] = acc0 + acc1;
+    __syncthreads();
+    if (wave != 0) return;
+    v4i sum = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) sum += part[w][lane];
+    const int col = n0 + (lane & 15);
+    if (col >= N) return;
+    const float sw = w_scale[col];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = (lane >> 4) * 4 + r;
+        if (row < M) {
+            const int a = sum[r] >> 8;
+            float y = static_cast<float>(a) * x_scale[row];
+            y = y * sw;
+            Y[static_cast<size_t>(row) * N + col] = y;
+            if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, hipStream_t s) {
+    if (M <= 16 && K % 128 == 0) {
+        dim3 grid(static_cast<unsigned>((N + 15) / 16));
+        if (acc_out)
+            hipLaunchKernelGGL((w4a4_gemm_m16<true>), grid, dim3(64 * kDecodeWaves), 0, s, Xq,
+                               x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+        else
+            hipLaunchKernelGGL((w4a4_gemm_m16<false>), grid, dim3(64 * kDecodeWaves), 0, s, Xq,
+                               x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+        return hipGetLastError();
+    }
     if (K % kStepCodes == 0) {
         const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
         dim3 grid(static_cast<unsigned>(tiles));

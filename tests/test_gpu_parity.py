@@ -116,6 +116,16 @@ def test_fwht_quant_orders(had_n, K, dtype):
     check_fwht_quant(x, had_n)
 
 
+@pytest.mark.parametrize("K", [32, 2048, 2080, 4096, 12288, 16384, 32768])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_fwht_quant_quant_only(K, dtype):
+    """had_n = 1 (rows already in the rotated basis): per-token INT4 only."""
+    rng = np.random.default_rng(K + 1)
+    x, _ = synth.outlier_activations(rng, 19, K, max(1, K // 1000), 100.0, dtype=dtype)
+    x[3] = 0
+    check_fwht_quant(x, 1)
+
+
 def test_fwht_quant_zero_and_tiny_rows():
     rng = np.random.default_rng(0)
     x = rng.standard_normal((6, 12288)).astype(np.float16)
@@ -235,6 +245,17 @@ def check_gemm(qx, qw, sx, sw, rows=None):
                                    (300, 200, 12288), (16, 4096, 4096), (129, 7, 192)])
 def test_gemm_ragged(M, N, K):
     rng = np.random.default_rng(M * N + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37, 128), (5, 4096 + 16, 4096), (16, 6144, 4096),
+                                   (16, 4096, 12288), (7, 24576, 4096), (16, 100, 384)])
+def test_gemm_decode_sizes(M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
     qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
     sx = rng.random(M).astype(np.float32)
