@@ -37,10 +37,36 @@ FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp
 KV_T, KV_H, KV_D = 4096, 32, 128
 KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
 
-# Traffic factors: measured HBM bytes per launch from rocprofv3 FETCH_SIZE /
-# WRITE_SIZE runs, each scaled by the same counters read on a plain copy of
-# known size.  None until the counters have been taken on the current kernels.
-TRAFFIC_BYTES = {"w4a4_gemm": None, "fwht_quant": None}
+# Measured HBM traffic per launch (bytes read, bytes written) from two
+# rocprofv3 passes (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) over
+# `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --copy-calibration`.
+# Each counter is scaled by what it reads for a 1 GiB device-to-device copy in
+# the same run: FETCH_SIZE reported 524313.75 KiB (factor 2.0), WRITE_SIZE
+# 1048576 KiB (factor 1.0).  A figure holds only for the kernel sources it was
+# taken on (SHA-256 prefixes below); after any change it reports null.
+CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
+TRAFFIC = {
+    "fwht_quant": {"sources": {"fwht_quant.hip": "4e0760921a90d1ef", "spin_device.h": "b6ac815ecffa4739"},
+                   "read": 100911871, "write": 25296896},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "de4ccc17334cb610", "spin_device.h": "b6ac815ecffa4739"},
+                  "read": 151262166, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "85c448c86afacada", "spin_device.h": "b6ac815ecffa4739"},
+                 "read": 33646256, "write": 8650752},
+}
+
+
+def traffic(kernel):
+    """Measured bytes per launch, or None if the kernel source has changed."""
+    import hashlib
+    entry = TRAFFIC[kernel]
+    for name, digest in entry["sources"].items():
+        try:
+            with open(os.path.join(CSRC, name), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                    return None
+        except OSError:
+            return None
+    return entry["read"] + entry["write"]
 
 
 def parse():
@@ -51,6 +77,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the qkv_proj GEMM and the decoder-layer chain measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     return ap.parse_args()
@@ -92,6 +120,86 @@ def cpu_baseline(x_host):
         "blas_threads": blas_threads,
         "omp_threads": omp,
     }
+
+
+def _time(fn, reps, stream):
+    """Mean milliseconds of fn() over `reps` launches, HIP events on `stream`."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def extra_workloads(args, dev, stream):
+    """qkv_proj (R1 folded, quant-only activations) and the decoder-layer linear
+    chain at M = 8192 and M = 16 (decode).  Folds run once, untimed."""
+    import torch
+    from rotation_bit_quantization_amd import spin, synth
+    out = {}
+    reps = max(5, args.steps // 2)
+
+    # qkv_proj: X 4096 x 4096 fp16 (residual in the R1 basis), W 4096 x 6144 folded with R1
+    q = synth.qkv_config()
+    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(q["w"]).to(dev), torch.from_numpy(q["r"]).to(dev), 4096)
+    X = torch.from_numpy(q["x"]).to(dev)
+    Xq, xs, _ = spin.spin_fwht_quant(X, 1)
+    Y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        spin.spin_w4a4_gemm(Xq, xs, Wq, ws, Y=Y)
+    t_q = _time(lambda i: spin.spin_fwht_quant(X, 1, Xq=Xq, x_scale=xs), reps, stream)
+    t_g = _time(lambda i: spin.spin_w4a4_gemm(Xq, xs, Wq, ws, Y=Y), reps, stream)
+    out["qkv_proj"] = {"workload": "X 4096x4096 fp16 quant-only, W 4096x6144 (R1 4096 folded), M=4096",
+                       "quant_us": t_q * 1e3, "gemm_us": t_g * 1e3,
+                       "gemm_tops": 2.0 * 4096 * 6144 * 4096 / (t_g * 1e-3) / 1e12,
+                       "gemm_frac_of_int8_peak": 2.0 * 4096 * 6144 * 4096 / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    del X, Xq, xs, Y, Wq, ws
+
+    # decoder-layer chain: qkv, o_proj (R2 128), gate/up (2 x 12288), down (H_12288)
+    c = synth.chain_config(M=8192)
+    layers = []
+    for name in ("qkv", "o", "gate_up", "down"):
+        L = c[name]
+        K, N = L["w"].shape
+        R = None if L["r"] is None else torch.from_numpy(L["r"]).to(dev)
+        _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(L["w"]).to(dev), R, L["r_block"])
+        layers.append({"name": name, "x": torch.from_numpy(L["x"]).to(dev), "K": K, "N": N,
+                       "had_n": L["had_n"], "wq": [Wq], "ws": [ws]})
+    torch.cuda.synchronize()
+
+    def chain(M, copy):
+        for L in layers:
+            xq, sc, _ = spin.spin_fwht_quant(L["x"][:M], L["had_n"], Xq=L["xq"][:M], x_scale=L["sc"][:M])
+            spin.spin_w4a4_gemm(xq, sc, L["wq"][copy], L["ws"][copy], Y=L["y"][:M])
+
+    for L in layers:
+        L["xq"] = torch.empty((8192, L["K"] // 2), dtype=torch.uint8, device=dev)
+        L["sc"] = torch.empty((8192,), dtype=torch.float32, device=dev)
+        L["y"] = torch.empty((8192, L["N"]), dtype=torch.float32, device=dev)
+    ops = 2.0 * 8192 * sum(L["K"] * L["N"] for L in layers)
+    for _ in range(2):
+        chain(8192, 0)
+    t8 = _time(lambda i: chain(8192, 0), max(3, reps // 3), stream)
+    out["chain_m8192"] = {"workload": "qkv + o_proj + gate/up + down (activation quant incl. R4 FWHT), M=8192",
+                          "us": t8 * 1e3, "tops": ops / (t8 * 1e-3) / 1e12,
+                          "frac_of_int8_peak": ops / (t8 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+
+    # decode, M = 16: weight bytes dominate; four weight copies rotate so they come from HBM
+    for L in layers:
+        for _ in range(3):
+            L["wq"].append(L["wq"][0].clone())
+            L["ws"].append(L["ws"][0].clone())
+    wbytes = sum(L["N"] * (L["K"] // 2 + 4) for L in layers)
+    for i in range(4):
+        chain(16, i)
+    t16 = _time(lambda i: chain(16, i % 4), 4 * max(3, reps // 3), stream)
+    out["chain_m16"] = {"workload": "same chain at M=16 (first 16 tokens), weights cold in HBM",
+                        "us": t16 * 1e3, "weight_GBps": wbytes / (t16 * 1e-3) / 1e9,
+                        "frac_of_hbm": wbytes / (t16 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    return out
 
 
 def main():
@@ -185,8 +293,12 @@ def main():
         kv_bytes = KV_T * KV_H * KV_BYTES_PER_GROUP
         extra["kv_quant"] = {"workload": "K [4096][32][128] fp16, H_128 + INT4, fp16 scale",
                              "us": k_s * 1e6, "GBps": kv_bytes / k_s / 1e9,
-                             "frac_of_hbm": kv_bytes / k_s / 1e9 / HBM_PEAK_GBPS}
+                             "frac_of_hbm": kv_bytes / k_s / 1e9 / HBM_PEAK_GBPS,
+                             "traffic": traffic("kv_quant")}
         del Kd, kc, ksc
+
+    if not args.no_extra:
+        extra.update(extra_workloads(args, dev, stream))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -219,11 +331,11 @@ def main():
         "gemm_frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
         "roofline": {"kernel": "w4a4_gemm", "bound": "mfma", "achieved": round(gemm_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": TRAFFIC_BYTES["w4a4_gemm"]},
+                     "traffic": traffic("w4a4_gemm")},
         "roofline_fwht_quant": {"kernel": "fwht_quant", "bound": "hbm", "achieved": round(fwht_gbps, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(fwht_gbps / HBM_PEAK_GBPS, 4),
-                                "traffic": TRAFFIC_BYTES["fwht_quant"]},
+                                "traffic": traffic("fwht_quant")},
         "parity_spot_code_mismatch": mism,
         "extra": extra,
     }
