@@ -178,13 +178,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // 16 bytes per lane from `src` into LDS at byte address lds_base + 16 * lane
-// (lds_base wave-uniform).  M0 is saved and restored around it; the only
-// register operand is the address, which the load consumes at issue.
+// (lds_base wave-uniform).  M0 is saved and restored around it, with the one
+// wait state an LDS DMA needs after an SALU write of M0; the only register
+// operand is the address, which the load consumes at issue.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
