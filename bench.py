@@ -199,6 +199,22 @@ def extra_workloads(args, dev, stream):
     out["chain_m16"] = {"workload": "same chain at M=16 (first 16 tokens), weights cold in HBM",
                         "us": t16 * 1e3, "weight_GBps": wbytes / (t16 * 1e-3) / 1e9,
                         "frac_of_hbm": wbytes / (t16 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+    # the same decode chain captured once per weight copy in a HIP graph and
+    # replayed: the eight launches no longer wait on the host
+    graphs = []
+    cap = torch.cuda.Stream()
+    for i in range(4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            chain(16, i)
+        graphs.append(g)
+    for i in range(4):
+        graphs[i].replay()
+    t16g = _time(lambda i: graphs[i % 4].replay(), 4 * max(3, reps // 3), stream)
+    out["chain_m16_graph"] = {"workload": "chain at M=16 as one HIP graph replay per token batch, weights cold",
+                              "us": t16g * 1e3, "weight_GBps": wbytes / (t16g * 1e-3) / 1e9,
+                              "frac_of_hbm": wbytes / (t16g * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     return out
 
 

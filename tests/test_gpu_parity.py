@@ -332,3 +332,50 @@ def test_repeat_runs_are_deterministic():
     X = _dev(cfg["x"])
     a = [_host(spin.spin_fwht_quant(X, 12288)[0]) for _ in range(3)]
     assert all(np.array_equal(a[0], b) for b in a[1:])
+
+
+def test_decode_chain_graph_replays_match_eager():
+    """A decode-sized chain (quant-only + GEMM, then FWHT-12288 + GEMM, M = 16)
+    captured in one HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager results bit for bit."""
+    rng = np.random.default_rng(7)
+    M = 16
+
+    def codes(r, c):
+        q = rng.integers(-7, 8, size=(r, c)).astype(np.int64)
+        return _dev(((q[:, 0::2] & 15) | ((q[:, 1::2] & 15) << 4)).astype(np.uint8))
+
+    xa = _dev(rng.standard_normal((M, 4096)).astype(np.float16))
+    xb = _dev(rng.standard_normal((M, 12288)).astype(np.float16))
+    wa, wsa = codes(1024, 4096), _dev(rng.random(1024).astype(np.float32))
+    wb, wsb = codes(512, 12288), _dev(rng.random(512).astype(np.float32))
+    bufs = {
+        "xqa": torch.empty((M, 2048), dtype=torch.uint8, device=DEV),
+        "sa": torch.empty((M,), dtype=torch.float32, device=DEV),
+        "ya": torch.empty((M, 1024), dtype=torch.float32, device=DEV),
+        "xqb": torch.empty((M, 6144), dtype=torch.uint8, device=DEV),
+        "sb": torch.empty((M,), dtype=torch.float32, device=DEV),
+        "yb": torch.empty((M, 512), dtype=torch.float32, device=DEV),
+    }
+
+    def chain():
+        spin.spin_fwht_quant(xa, 1, Xq=bufs["xqa"], x_scale=bufs["sa"])
+        spin.spin_w4a4_gemm(bufs["xqa"], bufs["sa"], wa, wsa, Y=bufs["ya"])
+        spin.spin_fwht_quant(xb, 12288, Xq=bufs["xqb"], x_scale=bufs["sb"])
+        spin.spin_w4a4_gemm(bufs["xqb"], bufs["sb"], wb, wsb, Y=bufs["yb"])
+
+    chain()
+    eager = {k: _host(v).copy() for k, v in bufs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        chain()
+    for rep in range(4):
+        for v in bufs.values():
+            v.fill_(0x5A if v.dtype == torch.uint8 else -1)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        for k, v in bufs.items():
+            assert np.array_equal(_host(v), eager[k]), f"replay {rep}: {k} differs from eager"
+    # and the eager quant-only codes are the oracle's (no rotation: exact)
+    pk, s_o, _ = oracle.fwht_quant(_host(xa), 1)
+    assert np.array_equal(pk, eager["xqa"]) and np.array_equal(s_o, eager["sa"])
