@@ -1,0 +1,105 @@
+"""Rotation-choice probe: W4A4 output error of one linear layer under many
+rotations (page "SpinQuant, Reproduced", Q3: randomised Hadamards against
+random orthogonal matrices, each a separate quantization of the same weights;
+the pages find the Hadamards better on average and tighter).
+
+For a rotation R of the layer's input space (the residual-stream rotation R1,
+folded on both sides), the layer computes X R . R^T W = X W in full precision
+(page "SpinQuant, Reproduced", Q1: computational invariance).  Quantized:
+
+    codes_x, s_x = per-token INT4 of X R     (spin_fold_rotation on X^T: its
+                                              output channels are the tokens)
+    codes_w, s_w = per-channel INT4 of R^T W (spin_fold_rotation on W)
+    Y            = spin_w4a4_gemm(codes_x, s_x, codes_w, s_w)
+    error        = ||Y - X W||_F / ||X W||_F  (X W exact, float64, on the host)
+
+Every step on the device is a libspin call; the host only builds inputs.  The
+randomised Hadamard is R = diag(s) H / sqrt(n): random signs on the input
+channels, then the Hadamard.  (Signs applied after the Hadamard, H diag(s),
+change nothing here: the per-token and per-channel absmax quantizers are
+symmetric, so those signs pass through the codes and cancel in the product.)
+The Hadamard itself comes from the library: folding the identity with
+R = NULL returns H^T / sqrt(n).
+
+    python -m rotation_bit_quantization_amd.probe [--tokens T] [--dim K] [--out N] [--draws D]
+"""
+
+import argparse
+import json
+import time
+
+import numpy as np
+import torch
+
+from . import spin, synth
+
+__all__ = ["library_hadamard", "w4a4_layer_error", "rotation_probe"]
+
+
+def library_hadamard(n, device="cuda"):
+    """H_n / sqrt(n) as a float32 [n][n] device tensor, from spin_fold_rotation
+    of the identity with the library Hadamard (which returns H^T / sqrt(n))."""
+    eye = torch.eye(n, dtype=torch.float32, device=device)
+    w_rot, _, _ = spin.spin_fold_rotation(eye, None, n)
+    return w_rot.t().contiguous()
+
+
+def w4a4_layer_error(x, w, r, y_ref):
+    """Relative Frobenius error of the W4A4 output of x . w with rotation r
+    (all float32 device tensors; y_ref the exact float64 product on the host).
+    Returns (error, device output Y)."""
+    K = x.shape[1]
+    _, xq, xs = spin.spin_fold_rotation(x.t().contiguous(), r, K)   # per-token codes of x r
+    _, wq, ws = spin.spin_fold_rotation(w, r, K)                    # per-channel codes of r^T w
+    y, _ = spin.spin_w4a4_gemm(xq, xs, wq, ws)
+    y64 = y.double().cpu().numpy()
+    return float(np.linalg.norm(y64 - y_ref) / np.linalg.norm(y_ref)), y
+
+
+def _stats(v):
+    v = np.asarray(v, np.float64)
+    return {"mean": float(v.mean()), "std": float(v.std()), "min": float(v.min()), "max": float(v.max()),
+            "n": int(v.size)}
+
+
+def rotation_probe(cfg=None, device="cuda"):
+    """Errors for: no rotation, the plain Hadamard, each randomised Hadamard
+    and each Haar rotation of ``cfg`` (``synth.probe_config()`` by default)."""
+    cfg = synth.probe_config() if cfg is None else cfg
+    x_h, w_h = cfg["x"], cfg["w"]
+    K = x_h.shape[1]
+    y_ref = x_h.astype(np.float64) @ w_h.astype(np.float64)
+    x = torch.from_numpy(x_h).to(device)
+    w = torch.from_numpy(w_h).to(device)
+    h = library_hadamard(K, device)
+    eye = torch.eye(K, dtype=torch.float32, device=device)
+    out = {"workload": {"tokens": int(x_h.shape[0]), "dim": int(K), "out": int(w_h.shape[1]),
+                        "draws": len(cfg["haar"])}}
+    out["none"] = w4a4_layer_error(x, w, eye, y_ref)[0]
+    out["hadamard"] = w4a4_layer_error(x, w, h, y_ref)[0]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    had = [w4a4_layer_error(x, w, torch.from_numpy(s).to(device)[:, None] * h, y_ref)[0] for s in cfg["signs"]]
+    haar = [w4a4_layer_error(x, w, torch.from_numpy(r).to(device), y_ref)[0] for r in cfg["haar"]]
+    torch.cuda.synchronize()
+    out["randomized_hadamard"] = _stats(had)
+    out["haar"] = _stats(haar)
+    out["seconds_per_rotation"] = (time.perf_counter() - t0) / (len(had) + len(haar))
+    out["errors"] = {"randomized_hadamard": had, "haar": haar}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--tokens", type=int, default=2048)
+    ap.add_argument("--dim", type=int, default=1024)
+    ap.add_argument("--out", type=int, default=1024)
+    ap.add_argument("--draws", type=int, default=32)
+    a = ap.parse_args()
+    res = rotation_probe(synth.probe_config(T=a.tokens, K=a.dim, N=a.out, draws=a.draws))
+    res.pop("errors")
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "outlier_activations", "gaussian_weight", "haar_orthogonal", "kv_heads",
-    "tiny_config", "down_config", "kv_config", "qkv_config", "chain_config",
+    "tiny_config", "down_config", "kv_config", "qkv_config", "chain_config", "probe_config",
 ]
 
 
@@ -134,3 +134,17 @@ def chain_config(seed=5, M=8192, hidden=4096, heads=32, head_dim=128, mlp=12288)
         out[name] = {"x": x, "w": w, "r": r, "r_block": r_block,
                      "had_n": K if name == "down" else 1}
     return out
+
+
+def probe_config(seed=6, T=2048, K=1024, N=1024, draws=32, n_outliers=8, mult=100.0):
+    """Rotation-choice probe on one synthetic layer (page "SpinQuant,
+    Reproduced", Q3: 32 randomised Hadamards against 32 random orthogonal
+    matrices on one layer): activations T x K float32 with ``n_outliers``
+    channels x ``mult``, weight K x N N(0, 0.02), ``draws`` Haar rotations of
+    order K and ``draws`` vectors of K random signs (+1 / -1)."""
+    rng = np.random.default_rng(seed)
+    x, idx = outlier_activations(rng, T, K, n_outliers, mult, dtype=np.float32)
+    w = gaussian_weight(rng, K, N)
+    haar = [haar_orthogonal(rng, K) for _ in range(draws)]
+    signs = [rng.choice(np.array([-1.0, 1.0], np.float32), size=K) for _ in range(draws)]
+    return {"x": x, "w": w, "haar": haar, "signs": signs, "outlier_idx": idx}

@@ -379,3 +379,54 @@ def test_decode_chain_graph_replays_match_eager():
     # and the eager quant-only codes are the oracle's (no rotation: exact)
     pk, s_o, _ = oracle.fwht_quant(_host(xa), 1)
     assert np.array_equal(pk, eager["xqa"]) and np.array_equal(s_o, eager["sa"])
+
+
+# ---------------------------------------------------------------- rotation-choice probe
+
+def test_library_hadamard_matches_oracle():
+    from rotation_bit_quantization_amd import probe
+    for n in (256, 768, 1024):
+        h = _host(probe.library_hadamard(n)).astype(np.float64)
+        ref = oracle.hadamard(n) / np.sqrt(np.float64(n))
+        assert np.abs(h - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_rotation_probe_matches_oracle():
+    """Every error the probe reports (no rotation, Hadamard, randomised
+    Hadamards diag(s) H, Haar rotations) equals the oracle's for the same float32
+    rotation within 1%, and one randomised-Hadamard layer output matches the
+    oracle elementwise (codes bit-exact up to near-tie flips)."""
+    from rotation_bit_quantization_amd import probe
+    cfg = synth.probe_config(T=64, K=256, N=128, draws=3)
+    res = probe.rotation_probe(cfg)
+    x, w = cfg["x"], cfg["w"]
+    K = x.shape[1]
+    y_ref = x.astype(np.float64) @ w.astype(np.float64)
+    H = (oracle.hadamard(K) / np.sqrt(np.float64(K))).astype(np.float32)
+
+    def run(R):
+        _, xq, xs = oracle.fold_rotation(np.ascontiguousarray(x.T), R, K)
+        _, wq, ws = oracle.fold_rotation(w, R, K)
+        y, _ = oracle.w4a4_gemm(xq, xs, wq, ws)
+        return y, xq, wq
+
+    def err(R):
+        y = run(R)[0].astype(np.float64)
+        return np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
+
+    assert abs(res["none"] - err(np.eye(K, dtype=np.float32))) <= 1e-2 * res["none"]
+    assert abs(res["hadamard"] - err(H)) <= 1e-2 * res["hadamard"]
+    for got, s in zip(res["errors"]["randomized_hadamard"], cfg["signs"]):
+        assert abs(got - err((s[:, None] * H).astype(np.float32))) <= 1e-2 * got
+    for got, r in zip(res["errors"]["haar"], cfg["haar"]):
+        assert abs(got - err(r)) <= 1e-2 * got
+    # elementwise, one randomised Hadamard
+    R = (cfg["signs"][0][:, None] * H).astype(np.float32)
+    y_o, xq_o, wq_o = run(R)
+    r_dev = _dev(R)
+    _, xq, xs = spin.spin_fold_rotation(_dev(np.ascontiguousarray(x.T)), r_dev, K)
+    _, wq, ws = spin.spin_fold_rotation(_dev(w), r_dev, K)
+    y, _ = spin.spin_w4a4_gemm(xq, xs, wq, ws)
+    fr = code_flips(_host(xq), xq_o, axis=1)
+    fc = code_flips(_host(wq), wq_o, axis=1)
+    assert_y_close(_host(y), y_o, flip_rows=fr, flip_cols=fc)
