@@ -218,6 +218,27 @@ def extra_workloads(args, dev, stream):
     return out
 
 
+def probe_workload(args):
+    """Rotation-choice probe on one synthetic layer (2048 tokens, 1024 -> 1024,
+    8 outlier channels x100): W4A4 error under 32 randomised Hadamards and 32
+    Haar rotations, each a fold of the activations and of the weights plus one
+    GEMM on the device; with the CPU leg, one rotation through the oracle."""
+    import oracle
+    from rotation_bit_quantization_amd import probe, synth
+    cfg = synth.probe_config()
+    res = probe.rotation_probe(cfg)
+    res.pop("errors")
+    res["workload"] = "one layer, 2048 tokens x 1024 -> 1024, 32 randomised Hadamards vs 32 Haar"
+    if not args.no_cpu_baseline:
+        x, w, r = cfg["x"], cfg["w"], cfg["haar"][0]
+        t0 = time.perf_counter()
+        _, xq, xs = oracle.fold_rotation(np.ascontiguousarray(x.T), r, x.shape[1])
+        _, wq, ws = oracle.fold_rotation(w, r, x.shape[1])
+        oracle.w4a4_gemm(xq, xs, wq, ws)
+        res["oracle_seconds_per_rotation"] = time.perf_counter() - t0
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -315,6 +336,9 @@ def main():
 
     if not args.no_extra:
         extra.update(extra_workloads(args, dev, stream))
+
+    if not args.no_extra:
+        extra["rotation_probe"] = probe_workload(args)
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

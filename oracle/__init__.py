@@ -21,7 +21,7 @@ Arithmetic conventions
 
 Modules
   hadamard  Sylvester / Paley-I / Kronecker Hadamard matrices, dense rotation
-  quant     per-row absmax INT4 quantizer, KV fp16-scale quantizer, nibble packing
+  quant     per-row absmax INT4 / INT8 quantizer, KV fp16-scale quantizer, nibble packing
   fold      W' = B^T W (B block-diagonal rotation) + per-output-channel INT4
   gemm      int64 GEMM on INT4 codes (C) + float32 dequant epilogue
   kv        head-wise Hadamard + per-(token, head) INT4 for the KV path
@@ -35,7 +35,7 @@ from .hadamard import sylvester, paley12, hadamard, rotate_rows, supported_had_n
 from .quant import (quantize_rows, quantize_kv_groups, pack_int4, unpack_int4,  # noqa: F401
                     quantize_given_scale)
 from .fold import fold_rotation, block_rotation  # noqa: F401
-from .gemm import gemm_int_codes, gemm_int_codes_blas, dequant, w4a4_gemm, gemm_rows  # noqa: F401
-from .kv import kv_quant  # noqa: F401
+from .gemm import gemm_int_codes, gemm_int_codes_blas, dequant, w4a4_gemm, w4a8_gemm, gemm_rows  # noqa: F401
+from .kv import kv_quant, kv_quant8  # noqa: F401
 from .stats import kurtosis_per_token, mean_kurtosis, orthogonality_error  # noqa: F401
-from .fwht_quant import fwht_quant  # noqa: F401
+from .fwht_quant import fwht_quant, fwht_quant8  # noqa: F401

@@ -17,7 +17,7 @@ import numpy as np
 from .hadamard import rotate_rows
 from .quant import quantize_rows, pack_int4
 
-__all__ = ["fwht_quant"]
+__all__ = ["fwht_quant", "fwht_quant8"]
 
 
 def fwht_quant(x, had_n: int):
@@ -31,3 +31,15 @@ def fwht_quant(x, had_n: int):
         y = rotate_rows(x, had_n).astype(np.float32)
     codes, scales = quantize_rows(y)
     return pack_int4(codes), scales, y
+
+
+def fwht_quant8(x, had_n: int):
+    """The 8-bit-activation variant (W4A8): the same rotation, then per-token
+    symmetric INT8 (``quantize_rows`` with qmax = 127), one code per byte.
+    Returns (codes int8 [M, K], scales float32 [M], y float32 [M, K])."""
+    x = np.asarray(x)
+    if x.ndim != 2:
+        raise ValueError("x must be [M, K]")
+    y = x.astype(np.float32) if had_n == 1 else rotate_rows(x, had_n).astype(np.float32)
+    codes, scales = quantize_rows(y, 127)
+    return codes, scales, y

@@ -20,7 +20,7 @@ import numpy as np
 from . import build as _build
 from .quant import unpack_int4
 
-__all__ = ["gemm_int_codes", "gemm_rows", "gemm_int_codes_blas", "dequant", "w4a4_gemm",
+__all__ = ["w4a8_gemm", "gemm_int_codes", "gemm_rows", "gemm_int_codes_blas", "dequant", "w4a4_gemm",
            "num_threads"]
 
 _lib = None
@@ -104,6 +104,16 @@ def dequant(acc, x_scale, w_scale) -> np.ndarray:
 def w4a4_gemm(Xq, x_scale, Wq, w_scale):
     """Full W4A4 product from packed operands: returns (Y float32 [M, N], acc int64)."""
     qx = unpack_int4(Xq)
+    qw = unpack_int4(Wq)
+    acc = gemm_int_codes(qx, qw)
+    return dequant(acc, x_scale, w_scale), acc
+
+
+def w4a8_gemm(Xq8, x_scale, Wq, w_scale):
+    """The W4A8 product: int8 activation codes [M, K] against packed INT4
+    weights [N, K/2]; int64 accumulation and the same float32 epilogue.
+    Returns (Y float32 [M, N], acc int64)."""
+    qx = np.asarray(Xq8, dtype=np.int8)
     qw = unpack_int4(Wq)
     acc = gemm_int_codes(qx, qw)
     return dequant(acc, x_scale, w_scale), acc

@@ -17,7 +17,7 @@ import numpy as np
 from .hadamard import rotate_rows
 from .quant import quantize_kv_groups, pack_int4
 
-__all__ = ["kv_quant"]
+__all__ = ["kv_quant", "kv_quant8"]
 
 
 def kv_quant(x, rotate: bool, quantize: bool = True):
@@ -38,3 +38,17 @@ def kv_quant(x, rotate: bool, quantize: bool = True):
         return None, None, y
     codes, s16 = quantize_kv_groups(y)
     return pack_int4(codes), s16, y
+
+
+def kv_quant8(x, rotate: bool, quantize: bool = True):
+    """The 8-bit KV variant (KV8): the same head-wise rotation, then per
+    (token, head) INT8 with an fp16 scale (``quantize_kv_groups`` with
+    qmax = 127).  Returns (codes int8 [T, H, D] | None, scales fp16 | None, y fp32)."""
+    x = np.asarray(x)
+    if x.ndim != 3:
+        raise ValueError("x must be [T, H, D]")
+    y = rotate_rows(x, x.shape[-1]).astype(np.float32) if rotate else x.astype(np.float32)
+    if not quantize:
+        return None, None, y
+    codes, s16 = quantize_kv_groups(y, 127)
+    return codes, s16, y

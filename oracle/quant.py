@@ -1,4 +1,4 @@
-"""Symmetric INT4 quantizers and nibble packing (oracle; test infrastructure).
+"""Symmetric INT4 / INT8 quantizers and nibble packing (oracle; test infrastructure).
 
 The pages (abstract; page "SpinQuant, Reproduced" Q7/Q8) quantize weights,
 activations and the KV cache to 4 bits but fix neither granularity, rounding,
@@ -15,6 +15,11 @@ clipping nor storage.  Readings taken here (one per decision):
   * two codes per byte, two's-complement nibbles, byte j holds code 2j in its
     low nibble and code 2j+1 in its high nibble.
 
+The 8-bit variant (W4A8KV8, named among the evaluated settings on page
+"SpinQuant, Reproduced", Q7) is read the same way with 127 in place of 7:
+s = fl32(a / 127), codes clamp(rne(fl32(y / s)), -127, 127), one signed byte
+per code; the KV scale is fp16_rne(fl32(a / 127)).
+
 All decisions are taken in float32 because float32 is what decides the integer.
 """
 
@@ -23,11 +28,8 @@ import numpy as np
 __all__ = ["quantize_rows", "quantize_given_scale", "quantize_kv_groups",
            "pack_int4", "unpack_int4"]
 
-_SEVEN = np.float32(7.0)
-
-
-def quantize_given_scale(y, s) -> np.ndarray:
-    """Codes rne(fl32(y / s)) clamped to [-7, 7], with s broadcast against y.
+def quantize_given_scale(y, s, qmax: int = 7) -> np.ndarray:
+    """Codes rne(fl32(y / s)) clamped to [-qmax, qmax], with s broadcast against y.
 
     ``y`` and ``s`` are float32.  Where s == 0 the codes are 0.
     """
@@ -37,37 +39,37 @@ def quantize_given_scale(y, s) -> np.ndarray:
         quot = np.divide(y32, s32, dtype=np.float32)          # IEEE float32 division
     quot = np.where(s32 == 0, np.float32(0), quot)
     q = np.rint(quot)                                         # round half to even
-    q = np.clip(q, -7, 7)
+    q = np.clip(q, -qmax, qmax)
     return q.astype(np.int8)
 
 
-def quantize_rows(y) -> tuple:
-    """Per-row symmetric INT4: returns (codes int8 [..., K], scales float32 [...]).
+def quantize_rows(y, qmax: int = 7) -> tuple:
+    """Per-row symmetric quantization: returns (codes int8 [..., K], scales float32 [...]).
 
-    a = max_i |y_i| over the last axis, s = fl32(a / 7), codes as in
-    ``quantize_given_scale``.  ``y`` must already be float32 (the exact values
-    whose quantization is being specified).
+    a = max_i |y_i| over the last axis, s = fl32(a / qmax) (qmax = 7 for INT4,
+    127 for INT8), codes as in ``quantize_given_scale``.  ``y`` must already be
+    float32 (the exact values whose quantization is being specified).
     """
     y32 = np.asarray(y, dtype=np.float32)
     a = np.max(np.abs(y32), axis=-1)
-    s = np.divide(a, _SEVEN, dtype=np.float32)
-    codes = quantize_given_scale(y32, s[..., None])
+    s = np.divide(a, np.float32(qmax), dtype=np.float32)
+    codes = quantize_given_scale(y32, s[..., None], qmax)
     return codes, s.astype(np.float32)
 
 
-def quantize_kv_groups(y) -> tuple:
-    """Per-group INT4 with an fp16 scale over the last axis.
+def quantize_kv_groups(y, qmax: int = 7) -> tuple:
+    """Per-group quantization with an fp16 scale over the last axis.
 
-    s16 = fp16 round-to-nearest-even of fl32(a / 7); codes
-    clamp(rne(fl32(y / float32(s16))), -7, 7); s16 == 0 -> codes 0.
+    s16 = fp16 round-to-nearest-even of fl32(a / qmax); codes
+    clamp(rne(fl32(y / float32(s16))), -qmax, qmax); s16 == 0 -> codes 0.
     Returns (codes int8, scales as float16).
     """
     y32 = np.asarray(y, dtype=np.float32)
     a = np.max(np.abs(y32), axis=-1)
-    s32 = np.divide(a, _SEVEN, dtype=np.float32)
+    s32 = np.divide(a, np.float32(qmax), dtype=np.float32)
     with np.errstate(over="ignore"):
         s16 = s32.astype(np.float16)                          # IEEE RNE float32 -> float16
-    codes = quantize_given_scale(y32, s16.astype(np.float32)[..., None])
+    codes = quantize_given_scale(y32, s16.astype(np.float32)[..., None], qmax)
     return codes, s16
 
 
