@@ -117,9 +117,10 @@ spin_status spin_fwht_quant(const void* X, spin_dtype x_dtype, int M, int K, int
  *   w_scale  [N] float32
  *   Y        [M][N] float32   OUTPUT: fl32(fl32(float(acc) * x_scale[m]) * w_scale[n])
  *   acc_out  [M][N] int32 or NULL   OUTPUT: acc[m][n] = sum_k qx[m][k] * qw[n][k]
- * The integer product is exact (int32 accumulation, bit-exact).
- * Requirements: M, N >= 0, K > 0, K % 64 == 0, K <= SPIN_GEMM_MAX_K; codes
- * must lie in [-8, 7] (any nibble is accepted).
+ * The integer product is exact (int32 accumulation, bit-exact) for codes in
+ * [-7, 7], the range the library produces; any nibble is accepted, and with
+ * -8 codes the bound on K that keeps the sum exact is 64/49 times smaller.
+ * Requirements: M, N >= 0, K > 0, K % 64 == 0, K <= SPIN_GEMM_MAX_K.
  */
 spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                            const float* w_scale, int M, int N, int K, float* Y,
@@ -143,6 +144,56 @@ spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_
  */
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
                           uint8_t* codes, uint16_t* scale, float* X_rot, void* stream);
+
+/*
+ * The 8-bit-activation variant, W4A8KV8 (page "SpinQuant, Reproduced", Q7
+ * lists it among the settings the paper evaluates): activations and KV
+ * vectors are quantized to symmetric INT8 with the same rules as above and
+ * 127 in place of 7 (s = fl32(max |y| / 127), codes clamp(rne(fl32(y / s)),
+ * -127, 127), one signed byte per code, natural order); weights stay INT4.
+ */
+
+/* Largest K spin_w4a8_gemm accepts: 127 * 7 * 16 * K must stay below 2^31
+   (weight codes are scaled by 16 in the int32 accumulation). */
+#define SPIN_GEMM8_MAX_K 150912
+
+/*
+ * spin_fwht_quant8 — spin_fwht_quant with per-token INT8 codes.
+ *
+ *   Xq8      [M][K] int8      OUTPUT: codes of y
+ *   x_scale  [M] float32      OUTPUT: s = fl32(max_k |y[m][k]| / 127)
+ * Every other argument, requirement and guarantee as for spin_fwht_quant.
+ */
+spin_status spin_fwht_quant8(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
+                             int8_t* Xq8, float* x_scale, float* X_rot, void* stream);
+
+/*
+ * spin_w4a8_gemm — INT8 activations x INT4 weights (W4A8).
+ *
+ *   Xq8      [M][K] int8      activation codes (from spin_fwht_quant8)
+ *   x_scale  [M] float32
+ *   Wq       [N][K/2] uint8   packed weight codes (from spin_fold_rotation)
+ *   w_scale  [N] float32
+ *   Y, acc_out as for spin_w4a4_gemm; the integer product is exact for
+ *   activation codes in [-127, 127] and weight codes in [-7, 7] (the ranges
+ *   the library produces).
+ * Requirements: M, N >= 0, K > 0, K % 128 == 0, K <= SPIN_GEMM8_MAX_K.
+ */
+spin_status spin_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_t* Wq,
+                           const float* w_scale, int M, int N, int K, float* Y,
+                           int32_t* acc_out, void* stream);
+
+/*
+ * spin_kv_quant8 — spin_kv_quant with INT8 KV codes (KV8).
+ *
+ *   codes   [T][H][D] int8 or NULL   OUTPUT: codes of y per (t, h)
+ *   scale   [T][H] uint16 (fp16 bits) or NULL   OUTPUT:
+ *           s16 = fp16_rne(fl32(max |y| / 127)); codes
+ *           clamp(rne(fl32(y / float(s16))), -127, 127), s16 == 0 gives zeros
+ * Every other argument, requirement and guarantee as for spin_kv_quant.
+ */
+spin_status spin_kv_quant8(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
+                           int8_t* codes, uint16_t* scale, float* X_rot, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* spin_status_string(spin_status s);

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspin.so")
-SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip"]
+SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip", "w4a8_gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kRowThreads = 256;
 
-template <typename TIn, bool WRITE_ROT>
+template <int BITS, typename TIn, bool WRITE_ROT>
 __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
     const TIn* __restrict__ X, int K, int log2p, int has12, int rotate, float norm,
     uint8_t* __restrict__ Xq, float* __restrict__ x_scale, float* __restrict__ X_rot) {
@@ -68,15 +68,21 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
     float mx = 0.0f;
     for (int i = tid; i < K; i += kRowThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(row[i]));
     const float amax = block_max_256(mx, red);
-    const float s = __fdiv_rn(amax, kSeven);
+    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
     if (tid == 0) x_scale[m] = s;
 
-    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * static_cast<size_t>(K / 2));
+    uint8_t* out = Xq + m * static_cast<size_t>(BITS == 4 ? K / 2 : K);
     for (int g = tid; g < K / 8; g += kRowThreads) {
         int c8[8];
+        if (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c8[j] = quant_exact(row[8 * g + j], s);
-        out[g] = pack8(c8);
+            for (int j = 0; j < 8; ++j) c8[j] = quant_exact(row[8 * g + j], s);
+            reinterpret_cast<uint32_t*>(out)[g] = pack8(c8);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c8[j] = quant_exact8(row[8 * g + j], s);
+            reinterpret_cast<uint2*>(out)[g] = make_uint2(pack4b(c8), pack4b(c8 + 4));
+        }
     }
     if (WRITE_ROT) {
         float* yr = X_rot + m * static_cast<size_t>(K);
@@ -137,9 +143,56 @@ __device__ __forceinline__ bool any_near_tie(const uint32_t* f) {
     return min(min(m01, m23), min(m45, m67)) < 3u;
 }
 
+// Codes of eight values z[k] whose true value is y_k = (z[k] * sg[k]) * norm,
+// stored at element e (a multiple of 8) of an output row: one dword of
+// nibbles (BITS = 4) or two dwords of bytes (BITS = 8).  The fast path (a
+// normal, moderate scale s) uses the magic-number estimate with the constant
+// c[k] = sg[k] * norm / s and falls back to the exact quotient near a tie.
+template <int BITS>
+__device__ __forceinline__ void quant8_store(uint8_t* row_out, int e, const float* z, const float* sg,
+                                             const float* c, float norm, float s, bool fast) {
+    if (BITS == 4) {
+        uint32_t word = 0;
+        bool exact = !fast;
+        if (fast) {
+            uint32_t f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], c[k], kQuantMagic));
+            word = pack8_magic(f);
+            exact = any_near_tie(f);
+        }
+        if (exact) {
+            int c8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c8[k] = quant_exact((z[k] * sg[k]) * norm, s);
+            word = pack8(c8);
+        }
+        *reinterpret_cast<uint32_t*>(row_out + e / 2) = word;
+    } else {
+        uint32_t w0 = 0, w1 = 0;
+        bool exact = !fast;
+        if (fast) {
+            uint32_t f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], c[k], kQuant8Magic));
+            w0 = pack4_magic8(f);
+            w1 = pack4_magic8(f + 4);
+            exact = any_near_tie8(f);
+        }
+        if (exact) {
+            int c8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c8[k] = quant_exact8((z[k] * sg[k]) * norm, s);
+            w0 = pack4b(c8);
+            w1 = pack4b(c8 + 4);
+        }
+        *reinterpret_cast<uint2*>(row_out + e) = make_uint2(w0, w1);
+    }
+}
+
 // One row per workgroup.  `one` is 1.0f passed at run time so that
 // (x0 * one + x1) stays a mixed-precision FMA reading both fp16 halves.
-template <bool WRITE_ROT>
+template <int BITS, bool WRITE_ROT>
 __global__ __launch_bounds__(256) void fwht_quant_k12288(
     const __half* __restrict__ X, float norm, float one, uint8_t* __restrict__ Xq,
     float* __restrict__ x_scale, float* __restrict__ X_rot) {
@@ -223,7 +276,7 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
 #pragma unroll
         for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(z[ci][k]));
     const float amax = block_max_256(mx, red) * norm;   // = max_i fl32(|z_i| * norm)
-    const float s = __fdiv_rn(amax, kSeven);
+    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
     if (tid == 0) x_scale[row] = s;
 
     // Sign of each held value relative to the true transform: phase 1 left
@@ -233,36 +286,18 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
     const float sg_lo = neg_lo ? -1.0f : 1.0f;        // registers k = 0..3 (b2 = 0)
     const float sg_hi = -sg_lo;                        // registers k = 4..7 (b2 = 1)
 
-    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * 6144 + (ch * 6) * 512 + (l16 * 64 + blo) / 2);
-    if ((s >= 0x1p-100f) && (s <= 0x1p+100f)) {
-        const float cr = norm * __fdiv_rn(1.0f, s);
-        const float cr_lo = sg_lo * cr, cr_hi = sg_hi * cr;
+    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288);
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    const float cr = fast ? norm * __fdiv_rn(1.0f, s) : 0.0f;
+    float sg[8], c[8];
 #pragma unroll
-        for (int ci = 0; ci < 6; ++ci) {
-            uint32_t f[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                f[k] = __float_as_uint(__builtin_fmaf(z[ci][k], k < 4 ? cr_lo : cr_hi, kQuantMagic));
-            uint32_t word = pack8_magic(f);
-            if (any_near_tie(f)) {
-                int c8[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    c8[k] = quant_exact((z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm, s);
-                word = pack8(c8);
-            }
-            out[ci * 128] = word;
-        }
-    } else {
-#pragma unroll
-        for (int ci = 0; ci < 6; ++ci) {
-            int c8[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                c8[k] = quant_exact((z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm, s);
-            out[ci * 128] = pack8(c8);
-        }
+    for (int k = 0; k < 8; ++k) {
+        sg[k] = k < 4 ? sg_lo : sg_hi;
+        c[k] = sg[k] * cr;
     }
+#pragma unroll
+    for (int ci = 0; ci < 6; ++ci)
+        quant8_store<BITS>(out, (ch * 6 + ci) * 1024 + l16 * 64 + blo, z[ci], sg, c, norm, s, fast);
     if (WRITE_ROT) {
         float* yr = X_rot + row * 12288 + (ch * 6) * 1024 + l16 * 64 + blo;
 #pragma unroll
@@ -298,7 +333,7 @@ __device__ __forceinline__ void load_chunk8<float>(const float* p, float* v) {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename TIn, int NCH, bool WRITE_ROT>
+template <int BITS, typename TIn, int NCH, bool WRITE_ROT>
 __global__ __launch_bounds__(256) void quant_rows(const TIn* __restrict__ X, int K,
                                                   uint8_t* __restrict__ Xq,
                                                   float* __restrict__ x_scale,
@@ -323,31 +358,18 @@ __global__ __launch_bounds__(256) void quant_rows(const TIn* __restrict__ X, int
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
         for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[i][k]));
-    const float s = __fdiv_rn(block_max_256(mx, red), kSeven);
+    const float s = __fdiv_rn(block_max_256(mx, red), BITS == 4 ? kSeven : kQmax8);
     if (tid == 0) x_scale[row] = s;
-    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + row * (K / 2));
+    uint8_t* out = Xq + row * static_cast<size_t>(BITS == 4 ? K / 2 : K);
     const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
     const float cr = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+    const float one[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+    const float crs[8] = {cr, cr, cr, cr, cr, cr, cr, cr};
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + 256 * i;
         if (c >= nch) break;
-        uint32_t word;
-        bool exact = !fast;
-        if (fast) {
-            uint32_t f[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(v[i][k], cr, kQuantMagic));
-            word = pack8_magic(f);
-            exact = any_near_tie(f);
-        }
-        if (exact) {
-            int c8[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) c8[k] = quant_exact(v[i][k], s);
-            word = pack8(c8);
-        }
-        out[c] = word;
+        quant8_store<BITS>(out, 8 * c, v[i], one, crs, 1.0f, s, fast);
         if (WRITE_ROT) {
             float4* yr = reinterpret_cast<float4*>(X_rot + row * K + 8 * c);
             yr[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
@@ -356,68 +378,75 @@ __global__ __launch_bounds__(256) void quant_rows(const TIn* __restrict__ X, int
     }
 }
 
-template <typename TIn, bool WR>
+template <int BITS, typename TIn, bool WR>
 hipError_t launch_quant_rows(const TIn* X, int M, int K, uint8_t* Xq, float* xs, float* Xr,
                              hipStream_t s) {
     const int nch = K / 8;
     if (nch <= 256)
-        hipLaunchKernelGGL((quant_rows<TIn, 1, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+        hipLaunchKernelGGL((quant_rows<BITS, TIn, 1, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
     else if (nch <= 512)
-        hipLaunchKernelGGL((quant_rows<TIn, 2, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+        hipLaunchKernelGGL((quant_rows<BITS, TIn, 2, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
     else if (nch <= 1024)
-        hipLaunchKernelGGL((quant_rows<TIn, 4, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+        hipLaunchKernelGGL((quant_rows<BITS, TIn, 4, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
     else
-        hipLaunchKernelGGL((quant_rows<TIn, 8, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
+        hipLaunchKernelGGL((quant_rows<BITS, TIn, 8, WR>), dim3(M), dim3(256), 0, s, X, K, Xq, xs, Xr);
     return hipGetLastError();
 }
 
-template <typename TIn, bool WR>
+template <int BITS, typename TIn, bool WR>
 hipError_t launch_rowlds(const TIn* X, int M, int K, HadOrder h, uint8_t* Xq, float* xs,
                          float* Xr, hipStream_t s) {
     const size_t lds = static_cast<size_t>(K) * sizeof(float);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwht_quant_rowlds<TIn, WR>),
+        reinterpret_cast<const void*>(&fwht_quant_rowlds<BITS, TIn, WR>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
     if (attr != hipSuccess) return attr;
     const float norm = (h.n > 1) ? static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(h.n))) : 1.0f;
-    hipLaunchKernelGGL((fwht_quant_rowlds<TIn, WR>), dim3(M), dim3(kRowThreads), lds, s, X, K,
+    hipLaunchKernelGGL((fwht_quant_rowlds<BITS, TIn, WR>), dim3(M), dim3(kRowThreads), lds, s, X, K,
                        h.log2p, h.has12 ? 1 : 0, h.n > 1 ? 1 : 0, norm, Xq, xs, Xr);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h, uint8_t* Xq,
-                             float* x_scale, float* X_rot, hipStream_t s) {
+template <int BITS>
+hipError_t launch_fwht_quant_bits(const void* X, bool x_f16, int M, int K, HadOrder h, uint8_t* Xq,
+                                  float* x_scale, float* X_rot, hipStream_t s) {
     if (x_f16 && h.n == 12288 && K == 12288) {
         const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
         const __half* x = static_cast<const __half*>(X);
         if (X_rot)
-            hipLaunchKernelGGL((fwht_quant_k12288<true>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288<BITS, true>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
                                x_scale, X_rot);
         else
-            hipLaunchKernelGGL((fwht_quant_k12288<false>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288<BITS, false>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
                                x_scale, X_rot);
         return hipGetLastError();
     }
     if (h.n == 1 && K <= 16384) {
         if (x_f16) {
             const __half* x = static_cast<const __half*>(X);
-            return X_rot ? launch_quant_rows<__half, true>(x, M, K, Xq, x_scale, X_rot, s)
-                         : launch_quant_rows<__half, false>(x, M, K, Xq, x_scale, X_rot, s);
+            return X_rot ? launch_quant_rows<BITS, __half, true>(x, M, K, Xq, x_scale, X_rot, s)
+                         : launch_quant_rows<BITS, __half, false>(x, M, K, Xq, x_scale, X_rot, s);
         }
         const float* x = static_cast<const float*>(X);
-        return X_rot ? launch_quant_rows<float, true>(x, M, K, Xq, x_scale, X_rot, s)
-                     : launch_quant_rows<float, false>(x, M, K, Xq, x_scale, X_rot, s);
+        return X_rot ? launch_quant_rows<BITS, float, true>(x, M, K, Xq, x_scale, X_rot, s)
+                     : launch_quant_rows<BITS, float, false>(x, M, K, Xq, x_scale, X_rot, s);
     }
     if (x_f16) {
         const __half* x = static_cast<const __half*>(X);
-        return X_rot ? launch_rowlds<__half, true>(x, M, K, h, Xq, x_scale, X_rot, s)
-                     : launch_rowlds<__half, false>(x, M, K, h, Xq, x_scale, X_rot, s);
+        return X_rot ? launch_rowlds<BITS, __half, true>(x, M, K, h, Xq, x_scale, X_rot, s)
+                     : launch_rowlds<BITS, __half, false>(x, M, K, h, Xq, x_scale, X_rot, s);
     }
     const float* x = static_cast<const float*>(X);
-    return X_rot ? launch_rowlds<float, true>(x, M, K, h, Xq, x_scale, X_rot, s)
-                 : launch_rowlds<float, false>(x, M, K, h, Xq, x_scale, X_rot, s);
+    return X_rot ? launch_rowlds<BITS, float, true>(x, M, K, h, Xq, x_scale, X_rot, s)
+                 : launch_rowlds<BITS, float, false>(x, M, K, h, Xq, x_scale, X_rot, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h, int bits, uint8_t* Xq,
+                             float* x_scale, float* X_rot, hipStream_t s) {
+    return bits == 8 ? launch_fwht_quant_bits<8>(X, x_f16, M, K, h, Xq, x_scale, X_rot, s)
+                     : launch_fwht_quant_bits<4>(X, x_f16, M, K, h, Xq, x_scale, X_rot, s);
 }
 
 }  // namespace spin

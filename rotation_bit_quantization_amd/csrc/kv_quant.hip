@@ -1,15 +1,16 @@
 // spin_kv_quant kernel: head-wise Hadamard H_128 / sqrt(128) (R3, page
 // "SpinQuant, Reproduced", Q5: the KV-path rotation runs online as a
 // Hadamard) and INT4 KV-cache codes with one fp16 scale per (token, head)
-// vector (abstract: 4-bit KV cache).
+// vector (abstract: 4-bit KV cache); BITS = 8 gives the KV8 variant (Q7 of the
+// same page names W4A8KV8 among the evaluated settings), one byte per code.
 //
 // Layout: one (token, head) vector of 128 values is owned by 16 lanes, 8
 // consecutive values each (a 16-byte fp16 load per lane, fully coalesced).
 // The three low index bits are butterflied in registers, the four high bits
 // across the 16 lanes of a DPP row (fused v_fmac_f32_dpp); the absmax is
 // reduced across the same 16 lanes with DPP.  Each lane then writes one dword
-// of 8 packed codes, so a vector's 64 code bytes are one contiguous 64-byte
-// store.  The normalisation 1/sqrt(128) is applied only where values are
+// of 8 packed codes (two dwords of byte codes at 8 bits), so a vector's code
+// bytes are one contiguous 64-byte (128-byte) store.  The normalisation 1/sqrt(128) is applied only where values are
 // written or quantized (folded into the quantizer constant).
 #include "spin_device.h"
 #include "spin_internal.h"
@@ -69,13 +70,28 @@ __device__ __forceinline__ uint32_t kv_codes(const float* z, float sign, float n
     return pack8(c8);
 }
 
+// The 8-bit variant of kv_codes: two dwords of byte codes.
+__device__ __forceinline__ uint2 kv_codes8(const float* z, float sign, float norm, float sf) {
+    if (sf >= 0x1p-14f && sf <= 65504.0f) {
+        const float cr = sign * (norm * __fdiv_rn(1.0f, sf));
+        uint32_t f[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], cr, kQuant8Magic));
+        if (!any_near_tie8(f)) return make_uint2(pack4_magic8(f), pack4_magic8(f + 4));
+    }
+    int c8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c8[k] = quant_exact8((z[k] * sign) * norm, sf);
+    return make_uint2(pack4b(c8), pack4b(c8 + 4));
+}
+
 // Two (token, head) vectors per 16-lane group: lane l holds values
 // 8 g(l) .. 8 g(l) + 7 of each, g the DPP-basis load permutation, so that the
 // four cross-lane butterfly levels (one v_fmac_f32_dpp each) leave lane l with
 // values 8 l .. 8 l + 7 of the transform times (-1)^popcount(l & 7).  The
 // first in-register level reads both fp16 halves with a mixed-precision FMA
 // (`one` = 1.0 passed at run time keeps it an FMA).
-template <typename TIn, bool ROTATE, bool QUANT, bool WRITE_ROT>
+template <int BITS, typename TIn, bool ROTATE, bool QUANT, bool WRITE_ROT>
 __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
     const TIn* __restrict__ X, long long groups, float norm, float one, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ scale, float* __restrict__ X_rot) {
@@ -158,50 +174,61 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
 #pragma unroll
             for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[p][k]));
             mx = row16_max(mx) * nrm;                 // = max_i fl32(|z_i| * norm)
-            const __half s16 = __float2half_rn(__fdiv_rn(mx, kSeven));
+            const __half s16 = __float2half_rn(__fdiv_rn(mx, BITS == 4 ? kSeven : kQmax8));
             const float sf = __half2float(s16);
-            reinterpret_cast<uint32_t*>(codes)[g * 16 + l] = kv_codes(v[p], sign, nrm, sf);
+            if (BITS == 4)
+                reinterpret_cast<uint32_t*>(codes)[g * 16 + l] = kv_codes(v[p], sign, nrm, sf);
+            else
+                reinterpret_cast<uint2*>(codes)[g * 16 + l] = kv_codes8(v[p], sign, nrm, sf);
             if (l == 0) scale[g] = __half_as_ushort(s16);
         }
     }
 }
 
-template <typename TIn, bool ROTATE, bool QUANT, bool WR>
+template <int BITS, typename TIn, bool ROTATE, bool QUANT, bool WR>
 hipError_t launch_kv_t(const TIn* X, long long groups, uint8_t* codes, uint16_t* scale,
                        float* Xr, hipStream_t s) {
     const float norm = static_cast<float>(1.0 / __builtin_sqrt(128.0));
     const long long per_block = 2LL * kKvGroupsPerBlock;
     const long long blocks = (groups + per_block - 1) / per_block;
-    hipLaunchKernelGGL((kv_quant_kernel<TIn, ROTATE, QUANT, WR>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((kv_quant_kernel<BITS, TIn, ROTATE, QUANT, WR>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kKvThreads), 0, s, X, groups, norm, 1.0f, codes, scale, Xr);
     return hipGetLastError();
 }
 
-template <typename TIn>
+template <int BITS, typename TIn>
 hipError_t launch_kv_dispatch(const TIn* X, long long groups, bool rotate, uint8_t* codes,
                               uint16_t* scale, float* Xr, hipStream_t s) {
     const bool quant = codes != nullptr;
     const bool wr = Xr != nullptr;
     if (rotate) {
-        if (quant) return wr ? launch_kv_t<TIn, true, true, true>(X, groups, codes, scale, Xr, s)
-                             : launch_kv_t<TIn, true, true, false>(X, groups, codes, scale, Xr, s);
-        return launch_kv_t<TIn, true, false, true>(X, groups, codes, scale, Xr, s);
+        if (quant) return wr ? launch_kv_t<BITS, TIn, true, true, true>(X, groups, codes, scale, Xr, s)
+                             : launch_kv_t<BITS, TIn, true, true, false>(X, groups, codes, scale, Xr, s);
+        return launch_kv_t<BITS, TIn, true, false, true>(X, groups, codes, scale, Xr, s);
     }
-    if (quant) return wr ? launch_kv_t<TIn, false, true, true>(X, groups, codes, scale, Xr, s)
-                         : launch_kv_t<TIn, false, true, false>(X, groups, codes, scale, Xr, s);
-    return launch_kv_t<TIn, false, false, true>(X, groups, codes, scale, Xr, s);
+    if (quant) return wr ? launch_kv_t<BITS, TIn, false, true, true>(X, groups, codes, scale, Xr, s)
+                         : launch_kv_t<BITS, TIn, false, true, false>(X, groups, codes, scale, Xr, s);
+    return launch_kv_t<BITS, TIn, false, false, true>(X, groups, codes, scale, Xr, s);
+}
+
+template <int BITS>
+hipError_t launch_kv_bits(const void* X, bool x_f16, long long groups, bool rotate, uint8_t* codes,
+                          uint16_t* scale, float* X_rot, hipStream_t s) {
+    if (x_f16)
+        return launch_kv_dispatch<BITS, __half>(static_cast<const __half*>(X), groups, rotate, codes,
+                                                scale, X_rot, s);
+    return launch_kv_dispatch<BITS, float>(static_cast<const float*>(X), groups, rotate, codes, scale,
+                                           X_rot, s);
 }
 
 }  // namespace
 
-hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, uint8_t* codes,
+hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, int bits, uint8_t* codes,
                            uint16_t* scale, float* X_rot, hipStream_t s) {
     const long long groups = static_cast<long long>(T) * H;
-    if (x_f16)
-        return launch_kv_dispatch<__half>(static_cast<const __half*>(X), groups, rotate, codes,
-                                          scale, X_rot, s);
-    return launch_kv_dispatch<float>(static_cast<const float*>(X), groups, rotate, codes, scale,
-                                     X_rot, s);
+    // rotate-only calls (no codes) are the same for either width
+    return bits == 8 && codes ? launch_kv_bits<8>(X, x_f16, groups, rotate, codes, scale, X_rot, s)
+                              : launch_kv_bits<4>(X, x_f16, groups, rotate, codes, scale, X_rot, s);
 }
 
 }  // namespace spin

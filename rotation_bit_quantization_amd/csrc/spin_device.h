@@ -25,6 +25,21 @@ __device__ __forceinline__ int quant_exact(float y, float s) {
     return static_cast<int>(q);
 }
 
+// The 8-bit variant (W4A8KV8): clamp(rne(fl32(y / s)), -127, 127).
+constexpr float kQmax8 = 127.0f;
+__device__ __forceinline__ int quant_exact8(float y, float s) {
+    if (s == 0.0f) return 0;
+    float q = __builtin_rintf(__fdiv_rn(y, s));
+    q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+    return static_cast<int>(q);
+}
+
+// Four signed byte codes (c[0] lowest) -> one little-endian dword.
+__device__ __forceinline__ uint32_t pack4b(const int* c) {
+    return (static_cast<uint32_t>(c[0]) & 0xFFu) | ((static_cast<uint32_t>(c[1]) & 0xFFu) << 8) |
+           ((static_cast<uint32_t>(c[2]) & 0xFFu) << 16) | ((static_cast<uint32_t>(c[3]) & 0xFFu) << 24);
+}
+
 // Eight codes (c[0] lowest) -> one little-endian dword of nibbles.
 __device__ __forceinline__ uint32_t pack8(const int* c) {
     uint32_t w = 0;
@@ -219,5 +234,31 @@ __device__ __forceinline__ void dpp_wht16(float* r, float s1, float s2, float s3
 constexpr float kQuantMagic = 192.5f + 0x1p-16f;
 
 __device__ __forceinline__ bool near_tie(uint32_t fbits) { return (fbits & 0xFFFFu) < 3u; }
+
+// 8-bit codes: f = fma(z, cr, kQuant8Magic) lands y/s + 1/2 on a grid of 2^-14
+// (f in [512, 1024) for |y/s| <= 127.5): bits 14..21 hold the two's-complement
+// byte of floor(y/s + 1/2), bits 0..13 the fraction, offset by two units so
+// that an exact tie reads 2.  The estimate of y/s is within ~0.7 units of
+// fl32(y / s) at |y/s| <= 127.5 (five float32 roundings of relative size 2^-24
+// at magnitude < 2^7), plus half a unit from rounding f itself; a fraction
+// below 5 units (two below a tie to three above) sends the code to the exact
+// IEEE quotient.
+constexpr float kQuant8Magic = 768.5f + 0x1p-13f;
+
+__device__ __forceinline__ bool near_tie8(uint32_t fbits) { return (fbits & 0x3FFFu) < 5u; }
+
+// Four 8-bit magic-number results -> one dword of codes (byte k from f[k]).
+__device__ __forceinline__ uint32_t pack4_magic8(const uint32_t* f) {
+    const uint32_t lo = __builtin_amdgcn_perm(f[1] << 2, f[0] << 2, 0x0c0c0602u);   // f0.b2, f1.b2
+    const uint32_t hi = __builtin_amdgcn_perm(f[3] << 2, f[2] << 2, 0x0c0c0602u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// True when any of eight 8-bit magic-number results is near a tie.
+__device__ __forceinline__ bool any_near_tie8(const uint32_t* f) {
+    const uint32_t m01 = min(f[0] & 0x3FFFu, f[1] & 0x3FFFu), m23 = min(f[2] & 0x3FFFu, f[3] & 0x3FFFu);
+    const uint32_t m45 = min(f[4] & 0x3FFFu, f[5] & 0x3FFFu), m67 = min(f[6] & 0x3FFFu, f[7] & 0x3FFFu);
+    return min(min(m01, m23), min(m45, m67)) < 5u;
+}
 
 }  // namespace spin

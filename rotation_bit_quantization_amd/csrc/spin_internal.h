@@ -14,15 +14,21 @@ struct HadOrder {
     bool has12;
 };
 
-hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h,
+// bits = 4: packed nibbles [M][K/2]; bits = 8: one signed byte per code [M][K].
+hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h, int bits,
                              uint8_t* Xq, float* x_scale, float* X_rot, hipStream_t s);
 
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, hipStream_t s);
 
-hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate,
+hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, int bits,
                            uint8_t* codes, uint16_t* scale, float* X_rot, hipStream_t s);
+
+// Int8 activation codes [M][K] against packed INT4 weights [N][K/2]; K % 128 == 0.
+hipError_t launch_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_t* Wq,
+                            const float* w_scale, int M, int N, int K, float* Y,
+                            int32_t* acc_out, hipStream_t s);
 
 hipError_t launch_fold_rotation(const float* W, int K, int N, const float* R, int r_block,
                                 HadOrder h, float* W_rot, uint8_t* Wq, float* w_scale,

@@ -11,6 +11,7 @@
 // times the true dot product (exact while 49 * K * 256 < 2^31); an arithmetic
 // shift by 8 recovers it exactly.  The k order inside a 64-wide MFMA step is
 // permuted identically on both sides, which leaves the dot product unchanged.
+#include "gemm_common.h"
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -20,15 +21,6 @@ namespace {
 constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBKBytes = 32;   // 64 codes per k-step
-
-__device__ __forceinline__ v4i widen16(uint2 p) {
-    v4i r;
-    r.x = static_cast<int>((p.x << 4) & 0xF0F0F0F0u);
-    r.y = static_cast<int>(p.x & 0xF0F0F0F0u);
-    r.z = static_cast<int>((p.y << 4) & 0xF0F0F0F0u);
-    r.w = static_cast<int>(p.y & 0xF0F0F0F0u);
-    return r;
-}
 
 // 128 x 128 output tile per workgroup of 4 waves (2 x 2), 64 x 64 per wave as
 // 4 x 4 MFMA 16x16x64 tiles.
@@ -144,55 +136,6 @@ constexpr int kStageBytes = 2 * kT * kStepBytes;   // A then B
 constexpr int kStages = 4;
 constexpr int kGemmThreads = 1024;
 constexpr int kGemmMinK = kStepCodes;
-
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ void tile_of(int bid, int tilesM, int tilesN, int* tm, int* tn) {
-    const int T = tilesM * tilesN;
-    int t = bid;
-    if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);    // contiguous block per XCD
-    constexpr int G = 4;                                        // tile rows per group
-    const int group = t / (G * tilesN);
-    const int first = group * G;
-    const int rows = min(G, tilesM - first);
-    const int r = t - group * G * tilesN;
-    *tm = first + r % rows;
-    *tn = r / rows;
-}
-
-__device__ __forceinline__ int slot_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-typedef const __attribute__((address_space(3))) void* lds_cptr;
-
-// Byte offset of a __shared__ object within the workgroup's LDS.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)(p)));
-}
-
-// s_waitcnt with only the vector-memory counter limited to n (n < 16).
-#define SPIN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((n) | 0x0F70)
-
-// Workgroup barrier that is also a compiler memory barrier (no load or store
-// moves across it) but, unlike __syncthreads, not a memory fence: it does not
-// wait for the LDS-DMA loads still in flight for later steps.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16 bytes per lane from `src` into LDS at byte address lds_base + 16 * lane
-// (lds_base wave-uniform).  M0 is saved and restored around it, with the one
-// wait state an LDS DMA needs after an SALU write of M0; the only register
-// operand is the address, which the load consumes at issue.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src), "s"(lds_base)
-        : "memory");
-}
 
 template <bool WRITE_ACC>
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(

@@ -17,13 +17,15 @@ import torch
 __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
-           "spin_w4a4_gemm", "spin_kv_quant", "EXPORTED_SYMBOLS"]
+           "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
+           "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
     SPIN_ERR_HIP = range(6)
 SPIN_F32, SPIN_F16 = 0, 1
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
+                    "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +58,11 @@ def load():
     lib.spin_fwht_quant.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a4_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
-    for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant"):
+    lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+    lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.spin_kv_quant8.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
+    for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
+                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.spin_status_string.argtypes = [ctypes.c_int]
     lib.spin_status_string.restype = ctypes.c_char_p
@@ -187,4 +193,69 @@ def spin_kv_quant(X, rotate, quantize=True, codes=None, scale=None, X_rot=None, 
     st = load().spin_kv_quant(_ptr(X), _dtype_code(X), T, H, D, int(rotate), _ptr(codes),
                               _ptr(scale), _ptr(X_rot), _stream(stream))
     _raise("spin_kv_quant", st)
+    return codes, scale, X_rot
+
+
+# ---------------------------------------------------------------- W4A8KV8 variant
+
+def spin_fwht_quant8(X, had_n, Xq8=None, x_scale=None, X_rot=None, want_rot=False, stream=None):
+    """X [M, K] fp16/fp32 -> (Xq8 [M, K] int8, x_scale [M] fp32, X_rot [M, K] fp32 or None)."""
+    _check(X, "X", (torch.float16, torch.float32))
+    M, K = X.shape
+    dev = X.device
+    Xq8 = torch.empty((M, K), dtype=torch.int8, device=dev) if Xq8 is None else Xq8
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    if X_rot is None and want_rot:
+        X_rot = torch.empty((M, K), dtype=torch.float32, device=dev)
+    _check(Xq8, "Xq8", (torch.int8,), (M, K))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    if X_rot is not None:
+        _check(X_rot, "X_rot", (torch.float32,), (M, K))
+    st = load().spin_fwht_quant8(_ptr(X), _dtype_code(X), M, K, int(had_n), _ptr(Xq8), _ptr(x_scale),
+                                 _ptr(X_rot), _stream(stream))
+    _raise("spin_fwht_quant8", st)
+    return Xq8, x_scale, X_rot
+
+
+def spin_w4a8_gemm(Xq8, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=False, stream=None):
+    """Int8 Xq8 [M, K], packed Wq [N, K/2] + scales -> (Y [M, N] fp32, acc [M, N] int32 or None)."""
+    _check(Xq8, "Xq8", (torch.int8,))
+    _check(Wq, "Wq", (torch.uint8,))
+    M, K = Xq8.shape
+    N, Kh = Wq.shape
+    if K != 2 * Kh:
+        raise ValueError("Xq8 and Wq disagree on K")
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    dev = Xq8.device
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev) if Y is None else Y
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    st = load().spin_w4a8_gemm(_ptr(Xq8), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K,
+                               _ptr(Y), _ptr(acc_out), _stream(stream))
+    _raise("spin_w4a8_gemm", st)
+    return Y, acc_out
+
+
+def spin_kv_quant8(X, rotate, quantize=True, codes=None, scale=None, X_rot=None, want_rot=False,
+                   stream=None):
+    """X [T, H, 128] fp16/fp32 -> (codes [T, H, 128] int8 | None, scale [T, H] fp16 | None, X_rot | None)."""
+    _check(X, "X", (torch.float16, torch.float32))
+    T, H, D = X.shape
+    dev = X.device
+    if quantize:
+        codes = torch.empty((T, H, D), dtype=torch.int8, device=dev) if codes is None else codes
+        scale = torch.empty((T, H), dtype=torch.float16, device=dev) if scale is None else scale
+        _check(codes, "codes", (torch.int8,), (T, H, D))
+        _check(scale, "scale", (torch.float16,), (T, H))
+    if X_rot is None and (want_rot or not quantize):
+        X_rot = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    if X_rot is not None:
+        _check(X_rot, "X_rot", (torch.float32,), (T, H, D))
+    st = load().spin_kv_quant8(_ptr(X), _dtype_code(X), T, H, D, int(rotate), _ptr(codes),
+                               _ptr(scale), _ptr(X_rot), _stream(stream))
+    _raise("spin_kv_quant8", st)
     return codes, scale, X_rot

@@ -118,3 +118,51 @@ def test_fold_validation(lib):
     assert call(K=256, r=96) == spin.SPIN_ERR_BAD_SHAPE           # K % r_block
     assert call(R=U) == spin.SPIN_ERR_MISALIGNED
     assert call(N=0) == spin.SPIN_OK
+
+
+def test_fwht_quant8_validation(lib):
+    f = lib.spin_fwht_quant8
+
+    def call(X=A, dt=spin.SPIN_F16, M=4, K=256, n=256, Xq=A, s=A, r=None):
+        return f(X, dt, M, K, n, Xq, s, r, None)
+
+    assert call(Xq=None) == spin.SPIN_ERR_NULL
+    assert call(n=3) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(K=48, n=1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(Xq=U) == spin.SPIN_ERR_MISALIGNED
+    assert call(M=0) == spin.SPIN_OK
+
+
+def test_w4a8_gemm_validation(lib):
+    f = lib.spin_w4a8_gemm
+
+    def call(Xq=A, sx=A, Wq=A, sw=A, M=16, N=16, K=256, Y=A, acc=None):
+        return f(Xq, sx, Wq, sw, M, N, K, Y, acc, None)
+
+    assert call(Xq=None) == spin.SPIN_ERR_NULL
+    assert call(sw=None) == spin.SPIN_ERR_NULL
+    assert call(K=64) == spin.SPIN_ERR_BAD_SHAPE                  # K % 128
+    assert call(K=150912 + 128) == spin.SPIN_ERR_BAD_SHAPE        # above SPIN_GEMM8_MAX_K
+    assert call(N=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(Xq=U) == spin.SPIN_ERR_MISALIGNED
+    assert call(M=0) == spin.SPIN_OK
+
+
+def test_kv_quant8_validation(lib):
+    f = lib.spin_kv_quant8
+
+    def call(X=A, dt=spin.SPIN_F16, T=4, H=2, D=128, rot=1, c=A, s=A, r=None):
+        return f(X, dt, T, H, D, rot, c, s, r, None)
+
+    assert call(s=None) == spin.SPIN_ERR_NULL
+    assert call(D=256) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(dt=3) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(c=U) == spin.SPIN_ERR_MISALIGNED
+    assert call(H=0) == spin.SPIN_OK
+
+
+def test_gemm8_bound_is_the_int32_limit():
+    """SPIN_GEMM8_MAX_K: the largest multiple of 128 with 127 * 7 * 16 * K < 2^31."""
+    k = 150912
+    assert k % 128 == 0 and 127 * 7 * 16 * k < 2 ** 31 and 127 * 7 * 16 * (k + 128) >= 2 ** 31
+    assert "#define SPIN_GEMM8_MAX_K 150912" in open(HEADER).read()
