@@ -218,6 +218,42 @@ def extra_workloads(args, dev, stream):
     return out
 
 
+def w4a8_workloads(args, dev, stream):
+    """The W4A8KV8 variant on the same shapes: fwht_quant8 + w4a8_gemm on the
+    down_proj workload (INT8 codes, 1 byte per element out) and kv_quant8 on K."""
+    import torch
+    from rotation_bit_quantization_amd import spin, synth
+    cfg = synth.down_config()
+    sets = max(1, args.sets)
+    X = [torch.from_numpy(cfg["x"]).to(dev)]
+    X += [X[0].clone() for _ in range(1, sets)]
+    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(cfg["w"]).to(dev), None, HAD_N)
+    q = [spin.spin_fwht_quant8(x, HAD_N) for x in X]
+    Y = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(sets)]
+    reps = max(10, args.steps)
+    for i in range(args.warmup):
+        spin.spin_w4a8_gemm(q[i % sets][0], q[i % sets][1], Wq, ws, Y=Y[i % sets])
+    t_f = _time(lambda i: spin.spin_fwht_quant8(X[i % sets], HAD_N, Xq8=q[i % sets][0], x_scale=q[i % sets][1]),
+                reps, stream)
+    t_g = _time(lambda i: spin.spin_w4a8_gemm(q[i % sets][0], q[i % sets][1], Wq, ws, Y=Y[i % sets]), reps, stream)
+    fbytes = M * (2 * K + K + 4)
+    out = {"workload": "fwht_quant8 X 4096x12288 fp16 (H12 x H1024, INT8 codes) + w4a8_gemm M=N=4096 K=12288",
+           "fwht_quant8_us": t_f * 1e3, "fwht_quant8_GBps": fbytes / (t_f * 1e-3) / 1e9,
+           "fwht_quant8_frac_of_hbm": fbytes / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "gemm_us": t_g * 1e3, "gemm_tops": 2.0 * M * N * K / (t_g * 1e-3) / 1e12,
+           "gemm_frac_of_int8_peak": 2.0 * M * N * K / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    del X, q, Y
+    kv = synth.kv_config()
+    Kd = torch.from_numpy(kv["k"]).to(dev)
+    codes = torch.empty((KV_T, KV_H, KV_D), dtype=torch.int8, device=dev)
+    sc = torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev)
+    t_k = _time(lambda i: spin.spin_kv_quant8(Kd, 1, codes=codes, scale=sc), reps, stream)
+    kbytes = KV_T * KV_H * (2 * KV_D + KV_D + 2)
+    out["kv_quant8_us"] = t_k * 1e3
+    out["kv_quant8_GBps"] = kbytes / (t_k * 1e-3) / 1e9
+    return out
+
+
 def probe_workload(args):
     """Rotation-choice probe on one synthetic layer (2048 tokens, 1024 -> 1024,
     8 outlier channels x100): W4A4 error under 32 randomised Hadamards and 32
@@ -338,6 +374,7 @@ def main():
         extra.update(extra_workloads(args, dev, stream))
 
     if not args.no_extra:
+        extra["w4a8kv8"] = w4a8_workloads(args, dev, stream)
         extra["rotation_probe"] = probe_workload(args)
 
     if args.copy_calibration:

@@ -26,6 +26,7 @@ Modules
   gemm      int64 GEMM on INT4 codes (C) + float32 dequant epilogue
   kv        head-wise Hadamard + per-(token, head) INT4 for the KV path
   stats     kurtosis and orthogonality error
+  cayley    Cayley update of an orthogonal matrix (rotation learning, offline)
 
 Parity pins live in ``tests/test_oracle_*.py``; every function here has at
 least one pin that does not re-use its own code.
@@ -39,3 +40,4 @@ from .gemm import gemm_int_codes, gemm_int_codes_blas, dequant, w4a4_gemm, w4a8_
 from .kv import kv_quant, kv_quant8  # noqa: F401
 from .stats import kurtosis_per_token, mean_kurtosis, orthogonality_error  # noqa: F401
 from .fwht_quant import fwht_quant, fwht_quant8  # noqa: F401
+from .cayley import skew_descent, cayley_step  # noqa: F401
