@@ -45,12 +45,13 @@ def library_hadamard(n, device="cuda"):
 
 
 def w4a4_layer_error(x, w, r, y_ref):
-    """Relative Frobenius error of the W4A4 output of x . w with rotation r
-    (all float32 device tensors; y_ref the exact float64 product on the host).
-    Returns (error, device output Y)."""
-    K = x.shape[1]
-    _, xq, xs = spin.spin_fold_rotation(x.t().contiguous(), r, K)   # per-token codes of x r
-    _, wq, ws = spin.spin_fold_rotation(w, r, K)                    # per-channel codes of r^T w
+    """Relative Frobenius error of the W4A4 output of x . w with rotation
+    blockdiag(r, ..., r) (all float32 device tensors, r of any order dividing
+    K; y_ref the exact float64 product on the host).  Returns (error, device
+    output Y)."""
+    rb = r.shape[0]
+    _, xq, xs = spin.spin_fold_rotation(x.t().contiguous(), r, rb)  # per-token codes of x B
+    _, wq, ws = spin.spin_fold_rotation(w, r, rb)                   # per-channel codes of B^T w
     y, _ = spin.spin_w4a4_gemm(xq, xs, wq, ws)
     y64 = y.double().cpu().numpy()
     return float(np.linalg.norm(y64 - y_ref) / np.linalg.norm(y_ref)), y

@@ -20,6 +20,7 @@ import numpy as np
 __all__ = [
     "outlier_activations", "gaussian_weight", "haar_orthogonal", "kv_heads",
     "tiny_config", "down_config", "kv_config", "qkv_config", "chain_config", "probe_config",
+    "r2_config",
 ]
 
 
@@ -148,3 +149,17 @@ def probe_config(seed=6, T=2048, K=1024, N=1024, draws=32, n_outliers=8, mult=10
     haar = [haar_orthogonal(rng, K) for _ in range(draws)]
     signs = [rng.choice(np.array([-1.0, 1.0], np.float32), size=K) for _ in range(draws)]
     return {"x": x, "w": w, "haar": haar, "signs": signs, "outlier_idx": idx}
+
+
+def r2_config(seed=7, T=512, heads=32, head_dim=128, N=1024, draws=32, n_out_per_head=2, mult=30.0):
+    """Learning R2 on one synthetic o_proj slice (page "SpinQuant, Reproduced",
+    Q5: one 128 x 128 rotation shared by the 32 heads, learned against the
+    layer's W4A4 output error, weights frozen): the value-path activations
+    T x (heads * head_dim) float32 with ``n_out_per_head`` outlier dims per head
+    x ``mult``, a weight (heads * head_dim) x N N(0, 0.02), and ``draws``
+    vectors of head_dim random signs for the random-Hadamard baselines."""
+    rng = np.random.default_rng(seed)
+    x = kv_heads(rng, T, heads, head_dim, n_out_per_head, mult, dtype=np.float32).reshape(T, heads * head_dim)
+    w = gaussian_weight(rng, heads * head_dim, N)
+    signs = [rng.choice(np.array([-1.0, 1.0], np.float32), size=head_dim) for _ in range(draws)]
+    return {"x": x, "w": w, "signs": signs, "heads": heads, "head_dim": head_dim}

@@ -430,3 +430,28 @@ def test_rotation_probe_matches_oracle():
     fr = code_flips(_host(xq), xq_o, axis=1)
     fc = code_flips(_host(wq), wq_o, axis=1)
     assert_y_close(_host(y), y_o, flip_rows=fr, flip_cols=fc)
+
+
+# ---------------------------------------------------------------- learned R2 (Cayley SGD)
+
+def test_r2_experiment_errors_match_oracle():
+    """The errors the R2 experiment measures through libspin (random
+    Hadamards and the learned rotation, block 128) equal the oracle's W4A4
+    layer error for the same float32 rotations within 1%."""
+    from rotation_bit_quantization_amd import cayley
+    cfg = synth.r2_config(T=128, heads=8, head_dim=128, N=256, draws=3)
+    res = cayley.r2_experiment(cfg, iters=8)
+    x, w = cfg["x"], cfg["w"]
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+
+    def err(R):
+        _, xq, xs = oracle.fold_rotation(np.ascontiguousarray(x.T), R, 128)
+        _, wq, ws = oracle.fold_rotation(w, R, 128)
+        y, _ = oracle.w4a4_gemm(xq, xs, wq, ws)
+        return np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+    H = oracle.hadamard(128) / np.sqrt(128.0)
+    draws = [err((s[:, None] * H).astype(np.float32)) for s in cfg["signs"]]
+    assert abs(res["random_hadamard"]["min"] - min(draws)) <= 1e-2 * min(draws)
+    assert abs(res["learned"] - err(res["R2"])) <= 1e-2 * res["learned"]
+    assert res["orthogonality_error"] < 1e-12
