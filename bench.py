@@ -34,6 +34,13 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
 M, K, N, HAD_N = 4096, 12288, 4096, 12288
 FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
+# fwht_quant_k12288 is bound by VALU issue, not by HBM: its fast path issues
+# 986 VALU instructions per thread for 48 elements (counted in the kernel's
+# ISA: 10 butterfly levels, the 50-operation H12, absmax, quantize and pack),
+# i.e. 20.54 lane-operations per element, against the chip's 256 CUs x 64
+# lanes x 2.4 GHz = 39.3 T lane-operations per second.
+FWHT_VALU_OPS_PER_ELEMENT = 986.0 / 48.0
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 KV_T, KV_H, KV_D = 4096, 32, 128
 KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
 
@@ -46,12 +53,12 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # taken on (SHA-256 prefixes below); after any change it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "4e0760921a90d1ef", "spin_device.h": "b6ac815ecffa4739"},
-                   "read": 100911871, "write": 25296896},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "de4ccc17334cb610", "spin_device.h": "b6ac815ecffa4739"},
-                  "read": 151262166, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "85c448c86afacada", "spin_device.h": "b6ac815ecffa4739"},
-                 "read": 33646256, "write": 8650752},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "df3771b15b858792", "spin_device.h": "d937b14287dd95c1"},
+                   "read": 100913798, "write": 25296896},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "902a6cfb8b318657", "gemm_common.h": "649caedacae11581", "spin_device.h": "d937b14287dd95c1"},
+                   "read": 151262643, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "a3506370fdcb50aa", "spin_device.h": "d937b14287dd95c1"},
+                   "read": 33646533, "write": 8650752},
 }
 
 
@@ -376,6 +383,11 @@ def main():
     if not args.no_extra:
         extra["w4a8kv8"] = w4a8_workloads(args, dev, stream)
         extra["rotation_probe"] = probe_workload(args)
+        from rotation_bit_quantization_amd import cayley
+        r2 = cayley.r2_experiment()
+        r2.pop("R2")
+        r2["workload"] = "R2 (128 x 128, 32 heads) learned by Cayley SGD on a 512-token o_proj slice, 120 iterations"
+        extra["r2_cayley"] = r2
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -413,6 +425,10 @@ def main():
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(fwht_gbps / HBM_PEAK_GBPS, 4),
                                 "traffic": traffic("fwht_quant")},
+        "roofline_fwht_quant_alu": {"kernel": "fwht_quant", "bound": "alu",
+                                    "achieved": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12, 2),
+                                    "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-op/s",
+                                    "frac": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12 / VALU_PEAK_TOPS, 4)},
         "parity_spot_code_mismatch": mism,
         "extra": extra,
     }

@@ -100,14 +100,14 @@ def r2_experiment(cfg=None, iters=120, lr=0.2, device="cuda"):
     x, w, heads, d = cfg["x"], cfg["w"], cfg["heads"], cfg["head_dim"]
     y_ref = x.astype(np.float64) @ w.astype(np.float64)
     xd, wd = torch.from_numpy(x).to(device), torch.from_numpy(w).to(device)
-    h = probe.library_hadamard(d, device)
-    draws = [torch.from_numpy(s).to(device)[:, None] * h for s in cfg["signs"]]
-    errs = [probe.w4a4_layer_error(xd, wd, r, y_ref)[0] for r in draws]
+    h = probe.library_hadamard(d, device).cpu().numpy()
+    draws = [np.ascontiguousarray(s[:, None] * h) for s in cfg["signs"]]
+    errs = [probe.w4a4_layer_error(xd, wd, torch.from_numpy(r).to(device), y_ref)[0] for r in draws]
     best = int(np.argmin(errs))
     t0 = time.perf_counter()
     # float64 start: the draw's signs over sqrt(d) (its float32 entries are
     # rounded, which the Cayley steps would otherwise carry along)
-    r0 = np.sign(draws[best].cpu().numpy().astype(np.float64)) / np.sqrt(np.float64(d))
+    r0 = np.sign(draws[best].astype(np.float64)) / np.sqrt(np.float64(d))
     R, hist = learn_r2(x, w, r0, heads, iters, lr)
     t_learn = time.perf_counter() - t0
     R32 = np.ascontiguousarray(R, dtype=np.float32)

@@ -13,7 +13,8 @@ folded on both sides), the layer computes X R . R^T W = X W in full precision
     Y            = spin_w4a4_gemm(codes_x, s_x, codes_w, s_w)
     error        = ||Y - X W||_F / ||X W||_F  (X W exact, float64, on the host)
 
-Every step on the device is a libspin call; the host only builds inputs.  The
+Every step on the device is a libspin call; the host builds the inputs (the
+rotations included) and measures the error; torch only moves memory.  The
 randomised Hadamard is R = diag(s) H / sqrt(n): random signs on the input
 channels, then the Hadamard.  (Signs applied after the Hadamard, H diag(s),
 change nothing here: the per-token and per-channel absmax quantizers are
@@ -39,9 +40,9 @@ __all__ = ["library_hadamard", "w4a4_layer_error", "rotation_probe"]
 def library_hadamard(n, device="cuda"):
     """H_n / sqrt(n) as a float32 [n][n] device tensor, from spin_fold_rotation
     of the identity with the library Hadamard (which returns H^T / sqrt(n))."""
-    eye = torch.eye(n, dtype=torch.float32, device=device)
+    eye = torch.from_numpy(np.eye(n, dtype=np.float32)).to(device)
     w_rot, _, _ = spin.spin_fold_rotation(eye, None, n)
-    return w_rot.t().contiguous()
+    return torch.from_numpy(np.ascontiguousarray(w_rot.cpu().numpy().T)).to(device)
 
 
 def w4a4_layer_error(x, w, r, y_ref):
@@ -53,7 +54,7 @@ def w4a4_layer_error(x, w, r, y_ref):
     _, xq, xs = spin.spin_fold_rotation(x.t().contiguous(), r, rb)  # per-token codes of x B
     _, wq, ws = spin.spin_fold_rotation(w, r, rb)                   # per-channel codes of B^T w
     y, _ = spin.spin_w4a4_gemm(xq, xs, wq, ws)
-    y64 = y.double().cpu().numpy()
+    y64 = y.cpu().numpy().astype(np.float64)
     return float(np.linalg.norm(y64 - y_ref) / np.linalg.norm(y_ref)), y
 
 
@@ -73,14 +74,16 @@ def rotation_probe(cfg=None, device="cuda"):
     x = torch.from_numpy(x_h).to(device)
     w = torch.from_numpy(w_h).to(device)
     h = library_hadamard(K, device)
-    eye = torch.eye(K, dtype=torch.float32, device=device)
+    h_host = h.cpu().numpy()
+    eye = torch.from_numpy(np.eye(K, dtype=np.float32)).to(device)
     out = {"workload": {"tokens": int(x_h.shape[0]), "dim": int(K), "out": int(w_h.shape[1]),
                         "draws": len(cfg["haar"])}}
     out["none"] = w4a4_layer_error(x, w, eye, y_ref)[0]
     out["hadamard"] = w4a4_layer_error(x, w, h, y_ref)[0]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    had = [w4a4_layer_error(x, w, torch.from_numpy(s).to(device)[:, None] * h, y_ref)[0] for s in cfg["signs"]]
+    had = [w4a4_layer_error(x, w, torch.from_numpy(s[:, None] * h_host).to(device), y_ref)[0]
+           for s in cfg["signs"]]
     haar = [w4a4_layer_error(x, w, torch.from_numpy(r).to(device), y_ref)[0] for r in cfg["haar"]]
     torch.cuda.synchronize()
     out["randomized_hadamard"] = _stats(had)
