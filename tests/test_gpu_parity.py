@@ -274,6 +274,20 @@ def test_gemm_extreme_accumulators():
     assert a[0, 0] == -49 * K and a[1, 0] == 49 * K
 
 
+@pytest.mark.parametrize("M", [3, 17])
+def test_gemm_largest_k(M):
+    """K = SPIN_GEMM_MAX_K = 171136 with every code at +-7: |acc| = 49 K, and the
+    kernels' internal 256-scaled sum 49 * 256 * K sits just below 2^31.  M = 3
+    takes the decode kernel, M = 17 the tiled one."""
+    K = 171136
+    qx = np.full((M, K), 7, np.int8)
+    qx[1] = -7
+    qw = np.full((2, K), 7, np.int8)
+    qw[1, K // 2:] = -7
+    _, a = check_gemm(qx, qw, np.ones(M, np.float32), np.ones(2, np.float32))
+    assert a[0, 0] == 49 * K and a[1, 0] == -49 * K and a[0, 1] == 0
+
+
 def test_gemm_down_config_shape_sampled():
     rng = np.random.default_rng(22)
     M, N, K = 4096, 4096, 12288
