@@ -49,28 +49,40 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --copy-calibration`.
 # Each counter is scaled by what it reads for a 1 GiB device-to-device copy in
 # the same run: FETCH_SIZE reported 524313.75 KiB (factor 2.0), WRITE_SIZE
-# 1048576 KiB (factor 1.0).  A figure holds only for the kernel sources it was
-# taken on (SHA-256 prefixes below); after any change it reports null.
+# 1048576 KiB (factor 1.0).  A figure holds only for the kernel code it was
+# taken on (SHA-256 prefixes of the sources without comments, below); after
+# any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "df3771b15b858792", "spin_device.h": "d937b14287dd95c1"},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "30651cff95824f4f", "spin_device.h": "812a2d84ab33d37f"},
                    "read": 100913798, "write": 25296896},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "902a6cfb8b318657", "gemm_common.h": "649caedacae11581", "spin_device.h": "d937b14287dd95c1"},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "c09491174ce56335", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "812a2d84ab33d37f"},
                    "read": 151262643, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "a3506370fdcb50aa", "spin_device.h": "d937b14287dd95c1"},
+    "kv_quant": {"sources": {"kv_quant.hip": "51391dd2ab5b766c", "spin_device.h": "812a2d84ab33d37f"},
                    "read": 33646533, "write": 8650752},
 }
 
 
-def traffic(kernel):
-    """Measured bytes per launch, or None if the kernel source has changed."""
+def source_digest(path):
+    """SHA-256 prefix of a C++/HIP source with its comments and blank lines
+    removed, so that only a change to the code itself invalidates a figure."""
     import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def traffic(kernel):
+    """Measured bytes per launch, or None if the kernel's code has changed."""
     entry = TRAFFIC[kernel]
     for name, digest in entry["sources"].items():
         try:
-            with open(os.path.join(CSRC, name), "rb") as f:
-                if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
-                    return None
+            if source_digest(os.path.join(CSRC, name)) != digest:
+                return None
         except OSError:
             return None
     return entry["read"] + entry["write"]

@@ -1,7 +1,10 @@
 // spin_fwht_quant kernels: online Hadamard of each activation row followed by
 // per-token symmetric INT4 (page "SpinQuant, Reproduced", Q5: R4 before
 // down_proj runs online as a Hadamard over the MLP width; abstract: 4-bit
-// activations).
+// activations).  Every kernel is templated on the code width BITS: 4 (codes
+// packed two per byte, scale max|y| / 7) or 8 (the W4A8 variant the same page
+// lists in Q7: one signed byte per code, scale max|y| / 127); only the
+// quantizer epilogue differs.
 //
 // fwht_quant_rowlds: one workgroup per row; the row is staged in LDS as
 // float32, normalised by fl32(1/sqrt(n)) on load, transformed by radix-2
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
 // Each DPP stage leaves lane i with (-1)^popcount(i & 7) times its value; both
 // signs, and nothing else, are folded into the per-thread quantizer constant.
 // The absmax is a block reduction; codes come from the magic-number quantizer
-// with an exact fallback near ties, eight per dword store.
+// with an exact fallback near ties (quant8_store), eight per store.
 constexpr int kLdsRowF = 68;                 // 64 floats + 4 pad
 constexpr int kLdsAF = 16 * kLdsRowF;        // one a (1024 b) = 16 padded rows
 constexpr int kLdsFloats12288 = 6 * kLdsAF;
@@ -313,11 +316,11 @@ __global__ __launch_bounds__(256) void fwht_quant_k12288(
 
 // ---------------------------------------------------------------------------
 // quant_rows: had_n = 1 (the rows are already in the rotated basis, e.g. R1
-// folded upstream): per-token INT4 only.  One workgroup of 256 threads per
-// row; thread t holds the chunks of 8 consecutive values t, t + 256, ...
-// (NCH of them, one 16-byte fp16 load each), so the row never leaves
-// registers: block absmax, then the magic-number quantizer with its exact
-// fallback near ties, one dword of codes per chunk.
+// folded upstream): per-token quantization only.  One workgroup of 256
+// threads per row; thread t holds the chunks of 8 consecutive values t,
+// t + 256, ... (NCH of them, one 16-byte fp16 load each), so the row never
+// leaves registers: block absmax, then the magic-number quantizer with its
+// exact fallback near ties, one store of codes per chunk.
 template <typename TIn>
 __device__ __forceinline__ void load_chunk8(const TIn* p, float* v);
 template <>
