@@ -163,7 +163,10 @@ def extra_workloads(args, dev, stream):
 
     # qkv_proj: X 4096 x 4096 fp16 (residual in the R1 basis), W 4096 x 6144 folded with R1
     q = synth.qkv_config()
-    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(q["w"]).to(dev), torch.from_numpy(q["r"]).to(dev), 4096)
+    from rotation_bit_quantization_amd import checks
+    r1 = torch.from_numpy(q["r"]).to(dev)
+    out["rotation_inputs_orthogonality"] = {"R1 Haar 4096 (qkv_proj)": checks.orthogonality_error(r1)}
+    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(q["w"]).to(dev), r1, 4096)
     X = torch.from_numpy(q["x"]).to(dev)
     Xq, xs, _ = spin.spin_fwht_quant(X, 1)
     Y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
@@ -184,6 +187,8 @@ def extra_workloads(args, dev, stream):
         L = c[name]
         K, N = L["w"].shape
         R = None if L["r"] is None else torch.from_numpy(L["r"]).to(dev)
+        if name == "o":
+            out["rotation_inputs_orthogonality"]["R2 Haar 128 (o_proj)"] = checks.orthogonality_error(R)
         _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(L["w"]).to(dev), R, L["r_block"])
         layers.append({"name": name, "x": torch.from_numpy(L["x"]).to(dev), "K": K, "N": N,
                        "had_n": L["had_n"], "wq": [Wq], "ws": [ws]})

@@ -469,3 +469,21 @@ def test_r2_experiment_errors_match_oracle():
     assert abs(res["random_hadamard"]["min"] - min(draws)) <= 1e-2 * min(draws)
     assert abs(res["learned"] - err(res["R2"])) <= 1e-2 * res["learned"]
     assert res["orthogonality_error"] < 1e-12
+
+
+def test_orthogonality_check_matches_oracle():
+    """checks.orthogonality_error (R^T R folded on the device) against the
+    oracle's float64 value, for every kind of R the harness feeds the fold,
+    and it flags a non-orthogonal input."""
+    from rotation_bit_quantization_amd import checks
+    rng = np.random.default_rng(9)
+    rs = [synth.haar_orthogonal(rng, 128), synth.haar_orthogonal(rng, 1024),
+          (oracle.hadamard(256) / np.sqrt(256.0)).astype(np.float32)]
+    for r in rs:
+        got = checks.orthogonality_error(_dev(r))
+        ref = oracle.orthogonality_error(r)
+        assert got <= ref + r.shape[0] * 2.0 ** -24 * 4
+    bad = rs[0].copy()
+    bad[3, 5] += 1e-3                                 # R^T R moves by ~2e-4
+    got, ref = checks.orthogonality_error(_dev(bad)), oracle.orthogonality_error(bad)
+    assert ref > 1e-4 and abs(got - ref) <= 1e-2 * ref
