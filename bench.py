@@ -34,12 +34,13 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
 M, K, N, HAD_N = 4096, 12288, 4096, 12288
 FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
-# fwht_quant_k12288 is bound by VALU issue, not by HBM: its fast path issues
-# 986 VALU instructions per thread for 48 elements (counted in the kernel's
-# ISA: 10 butterfly levels, the 50-operation H12, absmax, quantize and pack),
-# i.e. 20.54 lane-operations per element, against the chip's 256 CUs x 64
-# lanes x 2.4 GHz = 39.3 T lane-operations per second.
-FWHT_VALU_OPS_PER_ELEMENT = 986.0 / 48.0
+# The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2353.2
+# VALU instructions, 72 of them MFMA (rocprofv3 SQ_INSTS_VALU and
+# SQ_INSTS_MFMA over SQ_WAVES on the down_proj workload), so 2281.2 vector
+# lane-operations per lane for its 192 elements (the hi/lo split, the
+# 50-operation H12, absmax, quantize and pack): 11.88 per element, against
+# the chip's 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations per second.
+FWHT_VALU_OPS_PER_ELEMENT = (9638784.0 - 294912.0) / 4096.0 / 192.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 KV_T, KV_H, KV_D = 4096, 32, 128
 KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
@@ -48,18 +49,18 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # rocprofv3 passes (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) over
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --copy-calibration`.
 # Each counter is scaled by what it reads for a 1 GiB device-to-device copy in
-# the same run: FETCH_SIZE reported 524313.75 KiB (factor 2.0), WRITE_SIZE
+# the same run: FETCH_SIZE reported 524314.69 KiB (factor 2.0), WRITE_SIZE
 # 1048576 KiB (factor 1.0).  A figure holds only for the kernel code it was
 # taken on (SHA-256 prefixes of the sources without comments, below); after
 # any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "30651cff95824f4f", "spin_device.h": "812a2d84ab33d37f"},
-                   "read": 100913798, "write": 25296896},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "c09491174ce56335", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "812a2d84ab33d37f"},
-                   "read": 151262643, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "51391dd2ab5b766c", "spin_device.h": "812a2d84ab33d37f"},
-                   "read": 33646533, "write": 8650752},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "2523972a4b37e2fc", "spin_device.h": "c63f8fbd91ccf2df"},
+                   "read": 101781894, "write": 25296947},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "c09491174ce56335", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "c63f8fbd91ccf2df"},
+                   "read": 151262455, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "51391dd2ab5b766c", "spin_device.h": "c63f8fbd91ccf2df"},
+                   "read": 33646497, "write": 8650752},
 }
 
 
@@ -141,16 +142,76 @@ def cpu_baseline(x_host):
     }
 
 
+class HipEvents:
+    """Timing events of the HIP runtime the process already uses (PyTorch's),
+    created with hipEventDisableSystemFence: recording one then costs no
+    system-scope cache release, which with default events is paid at every
+    record and slows the kernels between them (the L2 is written back).
+    They are recorded on the stream the kernels are launched on."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self._ct = ctypes
+        self._hip = ctypes.CDLL(path or "libamdhip64.so.7")
+        self._made = []
+
+    def new(self):
+        ev = self._ct.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(self._ct.byref(ev), self._ct.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self._made.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        rc = self._hip.hipEventRecord(ev, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a, b):
+        out = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
+
+    def release(self):
+        for ev in self._made:
+            self._hip.hipEventDestroy(ev)
+        self._made = []
+
+
+_EVENTS = None
+
+
+def hip_events():
+    global _EVENTS
+    if _EVENTS is None:
+        _EVENTS = HipEvents()
+    return _EVENTS
+
+
 def _time(fn, reps, stream):
     """Mean milliseconds of fn() over `reps` launches, HIP events on `stream`."""
     import torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    he = hip_events()
+    ev = [[he.new() for _ in range(2)] for _ in range(reps)]
     for i in range(reps):
-        ev[i][0].record(stream)
+        he.record(ev[i][0], stream)
         fn(i)
-        ev[i][1].record(stream)
+        he.record(ev[i][1], stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    t = float(np.mean([he.ms(a, b) for a, b in ev]))
+    he.release()
+    return t
 
 
 def extra_workloads(args, dev, stream):
@@ -333,22 +394,24 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    he = hip_events()
+
     def step(i, ev=None):
         j = i % sets
         if ev is not None:
-            ev[0].record(stream)
+            he.record(ev[0], stream)
         spin.spin_fwht_quant(X[j], HAD_N, Xq=Xq[j], x_scale=xs[j])
         if ev is not None:
-            ev[1].record(stream)
+            he.record(ev[1], stream)
         spin.spin_w4a4_gemm(Xq[j], xs[j], Wq, ws, Y=Y[j])
         if ev is not None:
-            ev[2].record(stream)
+            he.record(ev[2], stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[he.new() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -356,8 +419,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    f_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    g_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    f_ms = np.array([he.ms(e[0], e[1]) for e in events])
+    g_ms = np.array([he.ms(e[1], e[2]) for e in events])
+    he.release()
     f_s, g_s = f_ms.mean() / 1e3, g_ms.mean() / 1e3
     fwht_bytes = M * FWHT_BYTES_PER_TOKEN
     fwht_gbps = fwht_bytes / f_s / 1e9
@@ -380,13 +444,8 @@ def main():
         ksc = [torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev) for _ in range(sets)]
         for i in range(args.warmup):
             spin.spin_kv_quant(Kd[i % sets], 1, codes=kc[i % sets], scale=ksc[i % sets])
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            kev[i][0].record(stream)
-            spin.spin_kv_quant(Kd[i % sets], 1, codes=kc[i % sets], scale=ksc[i % sets])
-            kev[i][1].record(stream)
-        torch.cuda.synchronize()
-        k_s = np.mean([e[0].elapsed_time(e[1]) for e in kev]) / 1e3
+        k_s = _time(lambda i: spin.spin_kv_quant(Kd[i % sets], 1, codes=kc[i % sets], scale=ksc[i % sets]),
+                    args.steps, stream) / 1e3
         kv_bytes = KV_T * KV_H * KV_BYTES_PER_GROUP
         extra["kv_quant"] = {"workload": "K [4096][32][128] fp16, H_128 + INT4, fp16 scale",
                              "us": k_s * 1e6, "GBps": kv_bytes / k_s / 1e9,

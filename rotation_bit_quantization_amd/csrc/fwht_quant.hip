@@ -12,6 +12,11 @@
 // by the order-12 mix across the 12 sub-blocks when n = 12 * 2^k, reduced to
 // its absmax, quantized with the exact IEEE quotient and packed.  It serves
 // every supported order and row length.
+//
+// fwht_quant_k12288_mfma: fp16 rows of 12288 with had_n = 12288 (the R4 /
+// down_proj case), one wave per row, the two 32-point stages of each
+// 1024-block on the matrix cores and the order-12 mix in registers (see the
+// kernel).
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -94,32 +99,7 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
 }
 
 // ---------------------------------------------------------------------------
-// fwht_quant_k12288: the R4 / down_proj case, fp16 rows of 12288 = 12 x 1024
-// with had_n = 12288.  Element i = a * 1024 + b; the transform is
-// Y = H12^T X H1024 on the 12 x 1024 view (x . (H12 (x) H1024)).
-//
-// One workgroup of 256 threads per row, two register layouts and one LDS
-// exchange:
-//   phase 1  thread holds x[a][4 beta + j] for all 12 a and j = 0..3
-//            (twelve 8-byte loads).  b bits 0-1 are butterflied in registers,
-//            the H12 mix runs in registers, b bits 2-5 are the low lane bits
-//            (four DPP levels); b bits 6-7 are lane bits 4-5, b bits 8-9 the
-//            wave.
-//   LDS      the rotated values are written in natural order, 64-float rows
-//            padded to 68 so that the phase-2 reads spread over the banks; the
-//            exchange runs in two rounds of six a each (26 KB of LDS per
-//            workgroup instead of 52 KB, so twice as many workgroups fit a CU).
-//   phase 2  thread holds 8 consecutive b (bits 0-2) for 6 of the 12 a: b bits
-//            6-9 are the low lane bits (four more DPP levels), b bits 3-4 lane
-//            bits 4-5, b bit 5 wave bit 0, the half of a wave bit 1.
-// Each DPP stage leaves lane i with (-1)^popcount(i & 7) times its value; both
-// signs, and nothing else, are folded into the per-thread quantizer constant.
-// The absmax is a block reduction; codes come from the magic-number quantizer
-// with an exact fallback near ties (quant8_store), eight per store.
-constexpr int kLdsRowF = 68;                 // 64 floats + 4 pad
-constexpr int kLdsAF = 16 * kLdsRowF;        // one a (1024 b) = 16 padded rows
-constexpr int kLdsFloats12288 = 6 * kLdsAF;
-
+// Quantizer epilogue shared by quant_rows and fwht_quant_k12288_mfma.
 __device__ __forceinline__ float h2f_lo(uint32_t w) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xFFFFu)));
 }
@@ -193,124 +173,250 @@ __device__ __forceinline__ void quant8_store(uint8_t* row_out, int e, const floa
     }
 }
 
-// One row per workgroup.  `one` is 1.0f passed at run time so that
-// (x0 * one + x1) stays a mixed-precision FMA reading both fp16 halves.
-template <int BITS, bool WRITE_ROT>
-__global__ __launch_bounds__(256) void fwht_quant_k12288(
-    const __half* __restrict__ X, float norm, float one, uint8_t* __restrict__ Xq,
-    float* __restrict__ x_scale, float* __restrict__ X_rot) {
-    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats12288];
-    __shared__ float red[4];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l16 = lane & 15;
-    const size_t row = blockIdx.x;
+// ---------------------------------------------------------------------------
+// fwht_quant_k12288_mfma: the R4 / down_proj case with the two 32-point
+// stages of H1024 = H32 (x) H32 on the matrix cores.  On the 32 x 32 view of
+// a 1024-block (x[32 i + c] = Xm[i][c]) the Sylvester transform is
+// Ym = H32 Xm H32, two products with a +-1 matrix:
+//   stage 1  T = Xm H32 with Xm as the A operand straight from the fp16 row
+//            (products of fp16 values with +-2^-5 are exact; float32 sums),
+//   stage 2  D = T^T H32, with T^T read from stage 1's accumulators, which
+//            already sit in A-operand order.  T is float32, so it enters as
+//            an fp16 pair hi + lo (hi = fp16(t), lo = fp16(t - hi)), two
+//            MFMAs whose sum carries 22 of t's 24 significant bits.
+// One wave per row keeps all twelve 1024-blocks in registers, so the H12 mix,
+// the absmax and the quantizer run without LDS or a barrier.
+//
+// Layouts (v_mfma_f32_32x32x16_f16): lane l = 32 h + c supplies row c of A
+// (column c of B) with k slots 8 h .. 8 h + 7; accumulator register r of lane
+// l holds row 8 (r / 4) + 4 h + r % 4, column c.  Lane l loads x[32 c + 16 h
+// .. + 15] (32 contiguous bytes) as k slots (c = 16 h + j, 16 h + 8 + j);
+// stage 1's columns are permuted by pi1(8 g + 4 h + s) = 16 h + 4 g + s, so
+// that after stage 2 register r of lane l holds element 32 c + 16 h + r:
+// sixteen consecutive elements per lane, one 8- or 16-byte store of codes.
+//
+// The 2^-5 on stage 1 keeps every fp16 hi in range for any finite fp16 row
+// (|t| <= 32 * 65504 * 2^-5).  The split loses at most 2^-25 absolute per
+// value, which is below 1e-5 of the row's absmax once that absmax (of y) is
+// at least 2.  Rows below that (and all-zero rows) are recomputed with stage
+// 1 scaled by 2^(m - 5), m = min(20, 29 - E), E the fp16 exponent field of the
+// row's largest |x|: that puts max |t| in [2^14, 2^15) for m < 20, and for
+// m = 20 every x is a multiple of 2^-24 of magnitude < 2^-6 (the split then
+// keeps 22 bits of the row's absmax or is exact).
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
-    // ---- phase 1: load x[a][4 beta .. 4 beta + 3], beta bits 0-3 permuted for DPP
-    const int beta_in = g_perm(l16) | ((lane >> 4) << 4) | (wave << 6);
-    uint2 raw[12];
-    {
-        const __half* xr = X + row * 12288 + 4 * beta_in;
-#pragma unroll
-        for (int a = 0; a < 12; ++a) {  // read once: non-temporal
-            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-            const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(xr + a * 1024));
-            raw[a] = make_uint2(t.x, t.y);
-        }
-    }
-    const float s1 = lane_sign(l16, 0b0101), s2 = lane_sign(l16, 0b0110);
-    const float s3 = lane_sign(l16, 0b1100), s4 = lane_sign(l16, 0b1000);
+__device__ __forceinline__ _Float16 sylvester_h(unsigned i, unsigned j, _Float16 mag) {
+    return (__builtin_popcount(i & j) & 1) ? -mag : mag;
+}
 
-    // b bits 0-1 in registers; the first level reads both fp16 halves directly
-    float v[12][4];
-#pragma unroll
-    for (int a = 0; a < 12; ++a) {
-        const uint32_t w0 = raw[a].x, w1 = raw[a].y;
-        const float s01 = __builtin_fmaf(h2f_lo(w0), one, h2f_hi(w0));
-        const float d01 = __builtin_fmaf(h2f_hi(w0), -one, h2f_lo(w0));
-        const float s23 = __builtin_fmaf(h2f_lo(w1), one, h2f_hi(w1));
-        const float d23 = __builtin_fmaf(h2f_hi(w1), -one, h2f_lo(w1));
-        v[a][0] = s01 + s23;
-        v[a][1] = d01 + d23;
-        v[a][2] = s01 - s23;
-        v[a][3] = d01 - d23;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float col[12];
-#pragma unroll
-        for (int a = 0; a < 12; ++a) col[a] = v[a][j];
-        h12_row(col);
-#pragma unroll
-        for (int a = 0; a < 12; ++a) v[a][j] = col[a];
-    }
-    dpp_wht16<48>(&v[0][0], s1, s2, s3, s4);
+__device__ __forceinline__ unsigned stage1_col(unsigned m) {
+    return ((m >> 2) & 1u) * 16u + (m >> 3) * 4u + (m & 3u);
+}
 
-    const int ch = wave >> 1;
-    const int blo = 8 * (((lane >> 4) & 3) | ((wave & 1) << 2));      // b & 63
-    float z[6][8];
-    const int beta = l16 | ((lane >> 4) << 4) | (wave << 6);
-    float* dst = lds + (beta >> 4) * kLdsRowF + 4 * l16;
-    const float* src = lds + g_perm(l16) * kLdsRowF + blo;
+// Splits eight float32 values t[r0 .. r0 + 7] into fp16 operands hi + lo:
+// hi = fp16(t) (packed by the compiler), lo = fp16(t - hi), the difference
+// exact in float32, one mixed-precision FMA with -1 per value reading its hi
+// half through op_sel.  The compiler does not track the VALU-write -> MFMA-read
+// dependency through inline asm, so the block ends with three wait states
+// (two are required before an MFMA may read a VGPR that a VALU wrote).  Its
+// inputs (the hi words) come from compiler-scheduled conversions that read the
+// stage-1 accumulators, so the MFMA-write -> VALU-read wait has already passed.
+__device__ __forceinline__ void split8(const f16v& t, int r0, float mone, h8v& hi, h8v& lo) {
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half) __syncthreads();
-#pragma unroll
-        for (int c = 0; c < 6; ++c)
-            *reinterpret_cast<float4*>(dst + c * kLdsAF) = make_float4(v[6*half+c][0], v[6*half+c][1], v[6*half+c][2], v[6*half+c][3]);
-        __syncthreads();
-        if (ch == half) {
-#pragma unroll
-            for (int ci = 0; ci < 6; ++ci) {
-                const float4 p = *reinterpret_cast<const float4*>(src + ci * kLdsAF);
-                const float4 q = *reinterpret_cast<const float4*>(src + ci * kLdsAF + 4);
-                z[ci][0] = p.x; z[ci][1] = p.y; z[ci][2] = p.z; z[ci][3] = p.w;
-                z[ci][4] = q.x; z[ci][5] = q.y; z[ci][6] = q.z; z[ci][7] = q.w;
-            }
-        }
+    for (int p = 0; p < 4; ++p) {
+        const h2v hp = {static_cast<_Float16>(t[r0 + 2 * p]), static_cast<_Float16>(t[r0 + 2 * p + 1])};
+        hw[p] = __builtin_bit_cast(uint32_t, hp);
     }
-    dpp_wht16<48>(&z[0][0], s1, s2, s3, s4);
+    asm("v_fma_mixlo_f16 %0, %4, %8, %9 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixlo_f16 %1, %5, %8, %11 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixlo_f16 %2, %6, %8, %13 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixlo_f16 %3, %7, %8, %15 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %4, %8, %10 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %1, %5, %8, %12 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %2, %6, %8, %14 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %3, %7, %8, %16 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "s_nop 2"
+        : "=&v"(lw[0]), "=&v"(lw[1]), "=&v"(lw[2]), "=&v"(lw[3])
+        : "v"(hw[0]), "v"(hw[1]), "v"(hw[2]), "v"(hw[3]), "s"(mone),
+          "v"(t[r0]), "v"(t[r0 + 1]), "v"(t[r0 + 2]), "v"(t[r0 + 3]),
+          "v"(t[r0 + 4]), "v"(t[r0 + 5]), "v"(t[r0 + 6]), "v"(t[r0 + 7]));
+    hi = __builtin_bit_cast(h8v, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    lo = __builtin_bit_cast(h8v, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
 
-    // ---- absmax of the row
+// y_block (unnormalised, times the stage-1 scale) = x_block . H1024.
+__device__ __forceinline__ f16v hadamard1024_mfma(const u4v& x0, const u4v& x1, const h8v& b1a,
+                                                  const h8v& b1b, const h8v& b2a, const h8v& b2b,
+                                                  float mone) {
+    const f16v zero = {};
+    f16v t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, x0), b1a, zero, 0, 0, 0);
+    t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, x1), b1b, t, 0, 0, 0);
+    h8v ha, la, hb, lb;
+    split8(t, 0, mone, ha, la);
+    split8(t, 8, mone, hb, lb);
+    f16v u = __builtin_amdgcn_mfma_f32_32x32x16_f16(la, b2a, zero, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_32x32x16_f16(lb, b2b, u, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, b2a, u, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_32x32x16_f16(hb, b2b, u, 0, 0, 0);
+    return u;
+}
+
+// The whole 12288-row: stage 1 (scaled by mag) and stage 2 per 1024-block,
+// then the H12 mix across the twelve blocks, in place in u.
+__device__ __forceinline__ void transform_row12288(const u4v (&raw)[12][2], _Float16 mag, const h8v& b2a,
+                                                   const h8v& b2b, float mone, f16v (&u)[12]) {
+    const int h = threadIdx.x >> 5, c = threadIdx.x & 31;
+    const unsigned col = stage1_col(c);
+    h8v b1a, b1b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        b1a[j] = sylvester_h(16 * h + j, col, mag);
+        b1b[j] = sylvester_h(16 * h + 8 + j, col, mag);
+    }
+#pragma unroll
+    for (int a = 0; a < 12; ++a) u[a] = hadamard1024_mfma(raw[a][0], raw[a][1], b1a, b1b, b2a, b2b, mone);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float col12[12];
+#pragma unroll
+        for (int a = 0; a < 12; ++a) col12[a] = u[a][r];
+        h12_row(col12);
+#pragma unroll
+        for (int a = 0; a < 12; ++a) u[a][r] = col12[a];
+    }
+}
+
+__device__ __forceinline__ float row_absmax(const f16v (&u)[12]) {
     float mx = 0.0f;
 #pragma unroll
-    for (int ci = 0; ci < 6; ++ci)
+    for (int a = 0; a < 12; ++a)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(z[ci][k]));
-    const float amax = block_max_256(mx, red) * norm;   // = max_i fl32(|z_i| * norm)
-    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
-    if (tid == 0) x_scale[row] = s;
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fabsf(u[a][r]));
+    return mx;
+}
 
-    // Sign of each held value relative to the true transform: phase 1 left
-    // (-1)^popcount(b2..b4), phase 2 (-1)^popcount(b6..b8); b2 is register bit 2.
-    const int b3 = (lane >> 4) & 1, b4 = (lane >> 5) & 1;
-    const bool neg_lo = ((b3 ^ b4) ^ (__builtin_popcount(l16 & 7) & 1)) != 0;
-    const float sg_lo = neg_lo ? -1.0f : 1.0f;        // registers k = 0..3 (b2 = 0)
-    const float sg_hi = -sg_lo;                        // registers k = 4..7 (b2 = 1)
+__device__ __forceinline__ float wave_max64(float v) {
+    v = row16_max(v);
+    v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
+    return __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
+}
 
-    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288);
-    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
-    const float cr = fast ? norm * __fdiv_rn(1.0f, s) : 0.0f;
-    float sg[8], c[8];
+// Sixteen consecutive codes from the magic-number quantizer (exact quotient
+// near a tie or outside the fast range), one store.
+template <int BITS>
+__device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float cr, float nrm, float s,
+                                              bool fast) {
+    if (BITS == 4) {
+        uint32_t w0 = 0, w1 = 0;
+        bool exact = !fast;
+        if (fast) {
+            uint32_t f[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        sg[k] = k < 4 ? sg_lo : sg_hi;
-        c[k] = sg[k] * cr;
-    }
-#pragma unroll
-    for (int ci = 0; ci < 6; ++ci)
-        quant8_store<BITS>(out, (ch * 6 + ci) * 1024 + l16 * 64 + blo, z[ci], sg, c, norm, s, fast);
-    if (WRITE_ROT) {
-        float* yr = X_rot + row * 12288 + (ch * 6) * 1024 + l16 * 64 + blo;
-#pragma unroll
-        for (int ci = 0; ci < 6; ++ci) {
-            float y[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) y[k] = (z[ci][k] * (k < 4 ? sg_lo : sg_hi)) * norm;
-            *reinterpret_cast<float4*>(yr + ci * 1024) = make_float4(y[0], y[1], y[2], y[3]);
-            *reinterpret_cast<float4*>(yr + ci * 1024 + 4) = make_float4(y[4], y[5], y[6], y[7]);
+            for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuantMagic));
+            w0 = pack8_magic(f);
+            w1 = pack8_magic(f + 8);
+            exact = any_near_tie(f) || any_near_tie(f + 8);
         }
+        if (exact) {
+            int c[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) c[k] = quant_exact(u[k] * nrm, s);
+            w0 = pack8(c);
+            w1 = pack8(c + 8);
+        }
+        *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+    } else {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        bool exact = !fast;
+        if (fast) {
+            uint32_t f[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuant8Magic));
+            w = make_uint4(pack4_magic8(f), pack4_magic8(f + 4), pack4_magic8(f + 8), pack4_magic8(f + 12));
+            exact = any_near_tie8(f) || any_near_tie8(f + 8);
+        }
+        if (exact) {
+            int c[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) c[k] = quant_exact8(u[k] * nrm, s);
+            w = make_uint4(pack4b(c), pack4b(c + 4), pack4b(c + 8), pack4b(c + 12));
+        }
+        *reinterpret_cast<uint4*>(p) = w;
+    }
+}
+
+// One wave (workgroup of 64) per row.
+template <int BITS, bool WRITE_ROT>
+__global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
+    const __half* __restrict__ X, float norm, float mone, uint8_t* __restrict__ Xq,
+    float* __restrict__ x_scale, float* __restrict__ X_rot) {
+    const int lane = threadIdx.x;
+    const int h = lane >> 5, c = lane & 31;
+    const size_t row = blockIdx.x;
+    const __half* xr = X + row * 12288 + 32 * c + 16 * h;
+
+    u4v raw[12][2];
+#pragma unroll
+    for (int a = 0; a < 12; ++a) {  // read once: non-temporal
+        raw[a][0] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + a * 1024));
+        raw[a][1] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + a * 1024 + 8));
+    }
+    h8v b2a, b2b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        b2a[j] = sylvester_h(8 * (j >> 2) + 4 * h + (j & 3), c, 1.0f16);
+        b2b[j] = sylvester_h(16 + 8 * (j >> 2) + 4 * h + (j & 3), c, 1.0f16);
+    }
+
+    f16v u[12];
+    float nrm = norm * 32.0f;
+    transform_row12288(raw, 0.03125f16, b2a, b2b, mone, u);
+    float amax = wave_max64(row_absmax(u)) * nrm;       // = max_i fl32(|u_i| * nrm)
+    if (!(amax >= 2.0f)) {
+        // small (or all-zero) row: reload it and rescale stage 1 from the
+        // exact largest |x|
+        u4v raw2[12][2];
+        uint32_t mb = 0;
+#pragma unroll
+        for (int a = 0; a < 12; ++a) {
+            raw2[a][0] = *reinterpret_cast<const u4v*>(xr + a * 1024);
+            raw2[a][1] = *reinterpret_cast<const u4v*>(xr + a * 1024 + 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                mb = max(mb, max(raw2[a][0][k] & 0x7FFFu, (raw2[a][0][k] >> 16) & 0x7FFFu));
+                mb = max(mb, max(raw2[a][1][k] & 0x7FFFu, (raw2[a][1][k] >> 16) & 0x7FFFu));
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), o, 64)));
+        const int m = min(20, 29 - static_cast<int>(mb >> 10));   // m >= -2 for any fp16 row
+        nrm = __builtin_ldexpf(norm, 5 - m);
+        transform_row12288(raw2, static_cast<_Float16>(__builtin_ldexpf(1.0f, m - 5)), b2a, b2b, mone, u);
+        amax = wave_max64(row_absmax(u)) * nrm;
+    }
+
+    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
+    if (lane == 0) x_scale[row] = s;
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    const float cr = fast ? nrm * __fdiv_rn(1.0f, s) : 0.0f;
+    const int e0 = 32 * c + 16 * h;
+    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288);
+#pragma unroll
+    for (int a = 0; a < 12; ++a)
+        quant16_store<BITS>(out + (a * 1024 + e0) * BITS / 8, u[a], cr, nrm, s, fast);
+    if (WRITE_ROT) {
+        float* yr = X_rot + row * 12288 + e0;
+#pragma unroll
+        for (int a = 0; a < 12; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(yr + a * 1024 + 4 * q) =
+                    make_float4(u[a][4 * q] * nrm, u[a][4 * q + 1] * nrm, u[a][4 * q + 2] * nrm,
+                                u[a][4 * q + 3] * nrm);
     }
 }
 
@@ -417,10 +523,10 @@ hipError_t launch_fwht_quant_bits(const void* X, bool x_f16, int M, int K, HadOr
         const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
         const __half* x = static_cast<const __half*>(X);
         if (X_rot)
-            hipLaunchKernelGGL((fwht_quant_k12288<BITS, true>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288_mfma<BITS, true>), dim3(M), dim3(64), 0, s, x, norm, -1.0f, Xq,
                                x_scale, X_rot);
         else
-            hipLaunchKernelGGL((fwht_quant_k12288<BITS, false>), dim3(M), dim3(256), 0, s, x, norm, 1.0f, Xq,
+            hipLaunchKernelGGL((fwht_quant_k12288_mfma<BITS, false>), dim3(M), dim3(64), 0, s, x, norm, -1.0f, Xq,
                                x_scale, X_rot);
         return hipGetLastError();
     }

@@ -131,13 +131,14 @@ namespace spin {
 // (A C)[1+b] = A[0] - S + A'[b] + 2 p_b.  Folding the + (u1 - u2) and
 // - (u1 + u2) terms in gives w1[1+b] = (U0 - S_U) + 2 (p_b(U) + u1[1+b]) and
 // w2[1+b] = (V0 - S_V) + 2 (p_b(V) - u2[1+b]).  50 adds / FMAs for 12 outputs
-// instead of 132.
-__device__ __forceinline__ void h12_row(float (&x)[12]) {
-    // u = x . P  (input permutation and signs)
-    const float u0 = x[0], u1 = x[1], u2 = x[2], u3 = -x[3], u4 = -x[5], u5 = -x[7];
-    const float u6 = -x[9], u7 = x[4], u8 = x[8], u9 = -x[6], u10 = x[10], u11 = -x[11];
-    const float U0 = u0 + u6, U1 = u1 + u7, U2 = u2 + u8, U3 = u3 + u9, U4 = u4 + u10, U5 = u5 + u11;
-    const float V0 = u0 - u6, V1 = u1 - u7, V2 = u2 - u8, V3 = u3 - u9, V4 = u4 - u10, V5 = u5 - u11;
+// instead of 132 (paley2_mix below).
+// w = u . H' for the Paley-II form H' = [[C + I, C - I], [C - I, -C - I]]
+// (see h12_row), in place: 50 adds / FMAs for 12 outputs.
+__device__ __forceinline__ void paley2_mix(float (&u)[12]) {
+    const float U0 = u[0] + u[6], U1 = u[1] + u[7], U2 = u[2] + u[8], U3 = u[3] + u[9], U4 = u[4] + u[10],
+                U5 = u[5] + u[11];
+    const float V0 = u[0] - u[6], V1 = u[1] - u[7], V2 = u[2] - u[8], V3 = u[3] - u[9], V4 = u[4] - u[10],
+                V5 = u[5] - u[11];
     // p_b over the five non-border entries, indices mod 5
     const float P0 = U2 + U5, P1 = U3 + U1, P2 = U4 + U2, P3 = U5 + U3, P4 = U1 + U4;
     const float SU = P0 + P1 + U4;
@@ -146,20 +147,28 @@ __device__ __forceinline__ void h12_row(float (&x)[12]) {
     const float SV = Q0 + Q1 + V4;
     const float EV = V0 - SV;
     const float w0 = SU + V0;
-    const float w1 = __builtin_fmaf(2.0f, P0 + u1, EU);
-    const float w2 = __builtin_fmaf(2.0f, P1 + u2, EU);
-    const float w3 = __builtin_fmaf(2.0f, P2 + u3, EU);
-    const float w4 = __builtin_fmaf(2.0f, P3 + u4, EU);
-    const float w5 = __builtin_fmaf(2.0f, P4 + u5, EU);
+    const float w1 = __builtin_fmaf(2.0f, P0 + u[1], EU);
+    const float w2 = __builtin_fmaf(2.0f, P1 + u[2], EU);
+    const float w3 = __builtin_fmaf(2.0f, P2 + u[3], EU);
+    const float w4 = __builtin_fmaf(2.0f, P3 + u[4], EU);
+    const float w5 = __builtin_fmaf(2.0f, P4 + u[5], EU);
     const float w6 = SV - U0;
-    const float w7 = __builtin_fmaf(2.0f, Q0 - u7, EV);
-    const float w8 = __builtin_fmaf(2.0f, Q1 - u8, EV);
-    const float w9 = __builtin_fmaf(2.0f, Q2 - u9, EV);
-    const float w10 = __builtin_fmaf(2.0f, Q3 - u10, EV);
-    const float w11 = __builtin_fmaf(2.0f, Q4 - u11, EV);
+    const float w7 = __builtin_fmaf(2.0f, Q0 - u[7], EV);
+    const float w8 = __builtin_fmaf(2.0f, Q1 - u[8], EV);
+    const float w9 = __builtin_fmaf(2.0f, Q2 - u[9], EV);
+    const float w10 = __builtin_fmaf(2.0f, Q3 - u[10], EV);
+    const float w11 = __builtin_fmaf(2.0f, Q4 - u[11], EV);
+    u[0] = w0; u[1] = w1; u[2] = w2; u[3] = w3; u[4] = w4; u[5] = w5;
+    u[6] = w6; u[7] = w7; u[8] = w8; u[9] = w9; u[10] = w10; u[11] = w11;
+}
+
+__device__ __forceinline__ void h12_row(float (&x)[12]) {
+    // u = x . P  (input permutation and signs)
+    float u[12] = {x[0], x[1], x[2], -x[3], -x[5], -x[7], -x[9], x[4], x[8], -x[6], x[10], -x[11]};
+    paley2_mix(u);
     // y = w . S  (output permutation and signs)
-    x[0] = w4;  x[1] = w11; x[2] = w0;  x[3] = w7;  x[4] = w5;   x[5] = w2;
-    x[6] = w1;  x[7] = w9;  x[8] = -w6; x[9] = w10; x[10] = w8;  x[11] = w3;
+    x[0] = u[4];  x[1] = u[11]; x[2] = u[0];  x[3] = u[7]; x[4] = u[5];   x[5] = u[2];
+    x[6] = u[1];  x[7] = u[9];  x[8] = -u[6]; x[9] = u[10]; x[10] = u[8]; x[11] = u[3];
 }
 
 }  // namespace spin

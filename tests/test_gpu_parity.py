@@ -136,6 +136,28 @@ def test_fwht_quant_zero_and_tiny_rows():
     assert s[1] == 0 and (xq[1] == 0).all()
 
 
+def magnitude_rows():
+    """fp16 rows of 12288 across the fp16 range: N(0,1) rows scaled by 2^e
+    (e = -30 rounds to zero, e = -26 leaves only subnormals and zeros), a constant 65504 row (every
+    32-sum of the first Hadamard stage reaches 32 * 65504), rows of random
+    +-65504, and rows whose rotated absmax sits near 2 (the matrix-core path
+    rescales rows below that)."""
+    rng = np.random.default_rng(11)
+    rows = [rng.standard_normal(12288) * 2.0 ** e for e in (-30, -26, -24, -20, -16, -12, -8, -4, -2, 0, 4, 8, 12)]
+    rows.append(np.full(12288, 65504.0))
+    rows += [np.where(rng.random(12288) < 0.5, -65504.0, 65504.0) for _ in range(2)]
+    base = rng.standard_normal(12288)
+    amax = np.abs(base @ oracle.hadamard(12288)).max() / np.sqrt(12288)
+    rows += [base * (f / amax) for f in (1.999, 2.0, 2.001)]
+    return np.stack(rows).astype(np.float16)
+
+
+def test_fwht_quant_12288_magnitude_range():
+    x = magnitude_rows()
+    xq, s, _ = check_fwht_quant(x, 12288)
+    assert ((s > 0) == (np.abs(x.astype(np.float32)).max(axis=1) > 0)).all()
+
+
 def test_fwht_quant_down_config_full_size():
     cfg = synth.down_config()
     rows = np.array([0, 1, 511, 2048, 4095])

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from rotation_bit_quantization_amd import spin, synth
-from tests.test_gpu_parity import _dev, _host, assert_rows_close, assert_y_close, code_flips
+from tests.test_gpu_parity import _dev, _host, assert_rows_close, assert_y_close, code_flips, magnitude_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,7 @@ def test_w4a8_down_chain_end_to_end_sampled():
     e8 = np.linalg.norm(_host(Y)[rows][:, cols] - y_ref) / np.linalg.norm(y_ref)
     e4 = np.linalg.norm(_host(Y4)[rows][:, cols] - y_ref) / np.linalg.norm(y_ref)
     assert e8 < e4
+
+
+def test_fwht_quant8_12288_magnitude_range():
+    check_fwht_quant8(magnitude_rows(), 12288)
