@@ -142,66 +142,11 @@ def cpu_baseline(x_host):
     }
 
 
-class HipEvents:
-    """Timing events of the HIP runtime the process already uses (PyTorch's),
-    created with hipEventDisableSystemFence: recording one then costs no
-    system-scope cache release, which with default events is paid at every
-    record and slows the kernels between them (the L2 is written back).
-    They are recorded on the stream the kernels are launched on."""
-
-    DISABLE_SYSTEM_FENCE = 0x20000000
-
-    def __init__(self):
-        import ctypes
-        path = None
-        with open("/proc/self/maps") as f:
-            for line in f:
-                if "libamdhip64" in line:
-                    path = line.split()[-1]
-                    break
-        self._ct = ctypes
-        self._hip = ctypes.CDLL(path or "libamdhip64.so.7")
-        self._made = []
-
-    def new(self):
-        ev = self._ct.c_void_p()
-        rc = self._hip.hipEventCreateWithFlags(self._ct.byref(ev), self._ct.c_uint(self.DISABLE_SYSTEM_FENCE))
-        if rc != 0:
-            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
-        self._made.append(ev)
-        return ev
-
-    def record(self, ev, stream):
-        rc = self._hip.hipEventRecord(ev, self._ct.c_void_p(stream.cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"hipEventRecord failed ({rc})")
-
-    def ms(self, a, b):
-        out = self._ct.c_float()
-        rc = self._hip.hipEventElapsedTime(self._ct.byref(out), a, b)
-        if rc != 0:
-            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-        return out.value
-
-    def release(self):
-        for ev in self._made:
-            self._hip.hipEventDestroy(ev)
-        self._made = []
-
-
-_EVENTS = None
-
-
-def hip_events():
-    global _EVENTS
-    if _EVENTS is None:
-        _EVENTS = HipEvents()
-    return _EVENTS
-
-
 def _time(fn, reps, stream):
-    """Mean milliseconds of fn() over `reps` launches, HIP events on `stream`."""
+    """Mean milliseconds of fn() over `reps` launches, HIP events (without the
+    system-scope fence) on `stream`."""
     import torch
+    from rotation_bit_quantization_amd.timing import hip_events
     he = hip_events()
     ev = [[he.new() for _ in range(2)] for _ in range(reps)]
     for i in range(reps):
@@ -212,6 +157,26 @@ def _time(fn, reps, stream):
     t = float(np.mean([he.ms(a, b) for a, b in ev]))
     he.release()
     return t
+
+
+def machine_ceilings(fwht_tbps, gemm_tops):
+    """Measured ceilings of this GPU (libspin_probe), reported beside the
+    published peaks that the roofline fractions use: the INT8 and FP16 MFMA
+    instructions the hot path issues, run back to back on the hot path's kind of
+    data by eight waves per CU, with the shader clock meanwhile, and a streaming
+    read of 2 GiB."""
+    from rotation_bit_quantization_amd import machine
+    i8 = machine.mfma_rate(0)
+    f16 = machine.mfma_rate(1)
+    rd = machine.read_bandwidth()
+    return {
+        "mfma_i32_32x32x32_i8": {"tops": round(i8["tops"], 1), "clock_ghz": round(i8["clock_ghz"], 3)},
+        "mfma_f32_32x32x16_f16": {"tflops": round(f16["tops"], 1), "clock_ghz": round(f16["clock_ghz"], 3)},
+        "hbm_read_tbps": round(rd["tbps"], 3),
+        "w4a4_gemm_frac_of_measured_int8": round(gemm_tops / i8["tops"], 4),
+        "fwht_quant_frac_of_measured_read": round(fwht_tbps / rd["tbps"], 4),
+        "note": "measured on this GPU; the roofline objects keep the published peaks",
+    }
 
 
 def extra_workloads(args, dev, stream):
@@ -394,6 +359,7 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    from rotation_bit_quantization_amd.timing import hip_events
     he = hip_events()
 
     def step(i, ev=None):
@@ -421,6 +387,18 @@ def main():
 
     f_ms = np.array([he.ms(e[0], e[1]) for e in events])
     g_ms = np.array([he.ms(e[1], e[2]) for e in events])
+    he.release()
+
+    # Warm figures, after and outside the timed region: every step reuses buffer
+    # set 0, so its activations (100 MB) come back from the Infinity Cache.
+    warm_ev = [[he.new() for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(0, warm_ev[i])
+    torch.cuda.synchronize()
+    warm = {"fwht_quant_us": float(np.median([he.ms(e[0], e[1]) for e in warm_ev])) * 1e3,
+            "gemm_us": float(np.median([he.ms(e[1], e[2]) for e in warm_ev])) * 1e3,
+            "note": "medians over the same number of steps with one buffer set (activations warm in the "
+                    "Infinity Cache); not the metric"}
     he.release()
     f_s, g_s = f_ms.mean() / 1e3, g_ms.mean() / 1e3
     fwht_bytes = M * FWHT_BYTES_PER_TOKEN
@@ -453,8 +431,10 @@ def main():
                              "traffic": traffic("kv_quant")}
         del Kd, kc, ksc
 
+    machine = None
     if not args.no_extra:
         extra.update(extra_workloads(args, dev, stream))
+        machine = machine_ceilings(M * FWHT_BYTES_PER_TOKEN / f_s / 1e12, gemm_tops)
 
     if not args.no_extra:
         extra["w4a8kv8"] = w4a8_workloads(args, dev, stream)
@@ -505,7 +485,13 @@ def main():
                                     "achieved": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12, 2),
                                     "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-op/s",
                                     "frac": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12 / VALU_PEAK_TOPS, 4)},
+        "launch_us": {name: {"mean": round(float(v.mean()) * 1e3, 3), "median": round(float(np.median(v)) * 1e3, 3),
+                             "p10": round(float(np.percentile(v, 10)) * 1e3, 3),
+                             "p90": round(float(np.percentile(v, 90)) * 1e3, 3)}
+                      for name, v in (("fwht_quant", f_ms), ("w4a4_gemm", g_ms))},
+        "warm": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in warm.items()},
         "parity_spot_code_mismatch": mism,
+        "machine": machine,
         "extra": extra,
     }
     if not args.no_cpu_baseline:

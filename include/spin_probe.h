@@ -1,0 +1,50 @@
+/*
+ * libspin_probe — machine probes that the benchmark reports beside the
+ * published peaks: the sustained dense MFMA rate of the two matrix
+ * instructions the hot path issues, the shader clock while the matrix cores
+ * are busy, and the streaming read bandwidth of HBM.  Not part of libspin and
+ * not used by it.  Calls for callers that measure the machine (bench.py).
+ *
+ * Conventions as in libspin.h: device pointers allocated by the caller,
+ * 16-byte aligned; `stream` is a hipStream_t as void*; arguments are checked on
+ * the host and nothing is enqueued when a check fails; the launch is
+ * asynchronous.
+ */
+#ifndef SPIN_PROBE_H
+#define SPIN_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "libspin.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Dense MFMA loop.  kind 0: v_mfma_i32_32x32x32_i8 (65536 ops each, the INT4
+ * GEMM's instruction); kind 1: v_mfma_f32_32x32x16_f16 (32768 flops each, the
+ * Hadamard stages).  `blocks` workgroups of 256 threads (4 waves); every wave
+ * runs `iters` rounds of four independent MFMAs, i.e. 4 * iters instructions.
+ * `operands`: 64 lanes x 8 dwords (A in dwords 0-3 of a lane, B in 4-7), the
+ * data the matrix cores multiply.  `timing`: 4 int64 per wave (blocks * 4
+ * waves): shader-cycle counter at start and end, 100 MHz real-time counter at
+ * start and end (the last word may be off by one: it also carries the
+ * accumulators so that no chain is optimised away).
+ * Errors: SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE (kind not 0/1, blocks or iters
+ * out of [1, 2^20] / [1, 2^24]), SPIN_ERR_MISALIGNED, SPIN_ERR_HIP. */
+spin_status spin_probe_mfma(int kind, int blocks, int iters, const uint32_t* operands, int64_t* timing,
+                            void* stream);
+
+/* Streaming read of `bytes` (a multiple of 16) from `buf` with non-temporal
+ * 16-byte loads by `blocks` workgroups of 256 threads in a grid-stride loop.
+ * `sink`: one uint32, written only if the data sum hits a fixed improbable
+ * value.  Errors: SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE (bytes 0 or not a multiple
+ * of 16, blocks out of [1, 2^20]), SPIN_ERR_MISALIGNED, SPIN_ERR_HIP. */
+spin_status spin_probe_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPIN_PROBE_H */

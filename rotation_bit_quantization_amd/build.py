@@ -1,10 +1,12 @@
-"""Build libspin.so in-tree with hipcc for gfx950.
+"""Build libspin.so (and the benchmark's machine probes, libspin_probe.so)
+in-tree with hipcc for gfx950.
 
     python -m rotation_bit_quantization_amd.build
 
 Each source is compiled to an object in parallel, then linked into
-``rotation_bit_quantization_amd/libspin.so``.  Every HIP source is compiled
-with the packed-fp32 VALU forms disabled.
+``rotation_bit_quantization_amd/libspin.so``; ``machine_probe.hip`` goes into
+``libspin_probe.so`` on its own.  Every HIP source is compiled with the
+packed-fp32 VALU forms disabled.
 """
 
 import concurrent.futures
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspin.so")
 SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip", "w4a8_gemm.hip"]
+PROBE_LIB = os.path.join(PKG, "libspin_probe.so")
+PROBE_SOURCES = ["machine_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -45,19 +49,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libspin.so; returns the library path."""
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libspin.so and libspin_probe.so; returns the
+    path of libspin.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
         print(LIB)
+        print(PROBE_LIB)
     return LIB
 
 

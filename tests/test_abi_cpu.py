@@ -166,3 +166,39 @@ def test_gemm8_bound_is_the_int32_limit():
     k = 150912
     assert k % 128 == 0 and 127 * 7 * 16 * k < 2 ** 31 and 127 * 7 * 16 * (k + 128) >= 2 ** 31
     assert "#define SPIN_GEMM8_MAX_K 150912" in open(HEADER).read()
+
+
+# ---------------------------------------------------------------- libspin_probe
+
+PROBE_HEADER = os.path.join(ROOT, "include", "spin_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe():
+    from rotation_bit_quantization_amd import machine
+    if not os.path.exists(machine.library_path()):
+        pytest.skip("libspin_probe.so not built (python -m rotation_bit_quantization_amd.build)")
+    return machine.load()
+
+
+def test_probe_header_declares_the_binding_symbols():
+    from rotation_bit_quantization_amd import machine
+    text = open(PROBE_HEADER).read()
+    declared = sorted(set(re.findall(r"^\s*spin_status\s+(spin_\w+)\s*\(", text, re.M)))
+    assert declared == sorted(machine.EXPORTED_SYMBOLS)
+
+
+def test_probe_symbols_and_validation(probe):
+    for name in ("spin_probe_mfma", "spin_probe_read"):
+        assert hasattr(probe, name)
+    NULL, BAD, MIS = 1, 2, 3
+    assert probe.spin_probe_mfma(0, 1, 1, None, A, None) == NULL
+    assert probe.spin_probe_mfma(2, 1, 1, A, A, None) == BAD
+    assert probe.spin_probe_mfma(0, 0, 1, A, A, None) == BAD
+    assert probe.spin_probe_mfma(1, 1, 0, A, A, None) == BAD
+    assert probe.spin_probe_mfma(0, 1, 1, U, A, None) == MIS
+    assert probe.spin_probe_read(None, 16, 1, A, None) == NULL
+    assert probe.spin_probe_read(A, 0, 1, A, None) == BAD
+    assert probe.spin_probe_read(A, 24, 1, A, None) == BAD
+    assert probe.spin_probe_read(A, 16, 0, A, None) == BAD
+    assert probe.spin_probe_read(U, 16, 1, A, None) == MIS
