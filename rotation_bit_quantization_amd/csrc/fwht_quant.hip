@@ -207,12 +207,22 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ _Float16 sylvester_h(unsigned i, unsigned j, _Float16 mag) {
-    return (__builtin_popcount(i & j) & 1) ? -mag : mag;
-}
-
-__device__ __forceinline__ unsigned stage1_col(unsigned m) {
-    return ((m >> 2) & 1u) * 16u + (m >> 3) * 4u + (m & 3u);
+// Sign bits of the +-1 B operands of both stages.  Slot j (bits j0 j1 j2) of
+// lane l = 32 h + c holds H32[i][col] with i = 8 (j / 4) + 4 h + j % 4, col = c
+// in stage 2 and i = 16 h + j, col = pi1(c) in stage 1 (plus 16, resp. 8, on i
+// for the second operand of the pair).  In both cases the parity of i & col
+// is the same function of the lane bits c0..c4:
+//   (h & c2) ^ (j0 & c0) ^ (j1 & c1) ^ (j2 & c3)   (^ c4 for the second operand)
+// sa / sb hold it at bit 15 (even j) and bit 31 (odd j) of dword j / 2.
+__device__ __forceinline__ void operand_signs(unsigned lane, u4v& sa, u4v& sb) {
+    const unsigned c = lane & 31u, h = lane >> 5;
+    const unsigned pair = 0x80008000u;
+    const unsigned m1 = (0u - ((c >> 1) & 1u)) & pair;
+    const unsigned m3 = (0u - ((c >> 3) & 1u)) & pair;
+    const unsigned m4 = (0u - ((c >> 4) & 1u)) & pair;
+    const unsigned base = ((0u - (h & (c >> 2) & 1u)) & pair) ^ (c << 31);
+    sa = u4v{base, base ^ m1, base ^ m3, base ^ m1 ^ m3};
+    sb = sa ^ m4;
 }
 
 // Splits eight float32 values t[r0 .. r0 + 7] into fp16 operands hi + lo:
@@ -267,16 +277,13 @@ __device__ __forceinline__ f16v hadamard1024_mfma(const u4v& x0, const u4v& x1, 
 
 // The whole 12288-row: stage 1 (scaled by mag) and stage 2 per 1024-block,
 // then the H12 mix across the twelve blocks, in place in u.
-__device__ __forceinline__ void transform_row12288(const u4v (&raw)[12][2], _Float16 mag, const h8v& b2a,
-                                                   const h8v& b2b, float mone, f16v (&u)[12]) {
-    const int h = threadIdx.x >> 5, c = threadIdx.x & 31;
-    const unsigned col = stage1_col(c);
-    h8v b1a, b1b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        b1a[j] = sylvester_h(16 * h + j, col, mag);
-        b1b[j] = sylvester_h(16 * h + 8 + j, col, mag);
-    }
+// The whole 12288-row: stage 1 (B entries +-mag, mag given by its fp16 bits
+// in both halves of magpair) and stage 2 per 1024-block, then the H12 mix
+// across the twelve blocks, in place in u.
+__device__ __forceinline__ void transform_row12288(const u4v (&raw)[12][2], unsigned magpair, const u4v& sa,
+                                                   const u4v& sb, float mone, f16v (&u)[12]) {
+    const h8v b1a = __builtin_bit_cast(h8v, sa | magpair), b1b = __builtin_bit_cast(h8v, sb | magpair);
+    const h8v b2a = __builtin_bit_cast(h8v, sa | 0x3C003C00u), b2b = __builtin_bit_cast(h8v, sb | 0x3C003C00u);
 #pragma unroll
     for (int a = 0; a < 12; ++a) u[a] = hadamard1024_mfma(raw[a][0], raw[a][1], b1a, b1b, b2a, b2b, mone);
 #pragma unroll
@@ -365,16 +372,12 @@ __global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
         raw[a][0] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + a * 1024));
         raw[a][1] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + a * 1024 + 8));
     }
-    h8v b2a, b2b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        b2a[j] = sylvester_h(8 * (j >> 2) + 4 * h + (j & 3), c, 1.0f16);
-        b2b[j] = sylvester_h(16 + 8 * (j >> 2) + 4 * h + (j & 3), c, 1.0f16);
-    }
+    u4v sa, sb;
+    operand_signs(lane, sa, sb);
 
     f16v u[12];
     float nrm = norm * 32.0f;
-    transform_row12288(raw, 0.03125f16, b2a, b2b, mone, u);
+    transform_row12288(raw, 0x28002800u, sa, sb, mone, u);     // +-2^-5
     float amax = wave_max64(row_absmax(u)) * nrm;       // = max_i fl32(|u_i| * nrm)
     if (!(amax >= 2.0f)) {
         // small (or all-zero) row: reload it and rescale stage 1 from the
@@ -395,7 +398,8 @@ __global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
         for (int o = 1; o < 64; o <<= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), o, 64)));
         const int m = min(20, 29 - static_cast<int>(mb >> 10));   // m >= -2 for any fp16 row
         nrm = __builtin_ldexpf(norm, 5 - m);
-        transform_row12288(raw2, static_cast<_Float16>(__builtin_ldexpf(1.0f, m - 5)), b2a, b2b, mone, u);
+        const unsigned mag = __builtin_bit_cast(unsigned short, static_cast<_Float16>(__builtin_ldexpf(1.0f, m - 5)));
+        transform_row12288(raw2, mag * 0x10001u, sa, sb, mone, u);
         amax = wave_max64(row_absmax(u)) * nrm;
     }
 
