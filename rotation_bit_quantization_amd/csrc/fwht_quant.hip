@@ -326,7 +326,7 @@ __device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float c
             for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuantMagic));
             w0 = pack8_magic(f);
             w1 = pack8_magic(f + 8);
-            exact = any_near_tie(f) || any_near_tie(f + 8);
+            exact = any_near_tie(f) | any_near_tie(f + 8);   // no short circuit: one branch
         }
         if (exact) {
             int c[16];
@@ -344,7 +344,7 @@ __device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float c
 #pragma unroll
             for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuant8Magic));
             w = make_uint4(pack4_magic8(f), pack4_magic8(f + 4), pack4_magic8(f + 8), pack4_magic8(f + 12));
-            exact = any_near_tie8(f) || any_near_tie8(f + 8);
+            exact = any_near_tie8(f) | any_near_tie8(f + 8);
         }
         if (exact) {
             int c[16];
@@ -407,11 +407,10 @@ __global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
     if (lane == 0) x_scale[row] = s;
     const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
     const float cr = fast ? nrm * __fdiv_rn(1.0f, s) : 0.0f;
-    const int e0 = 32 * c + 16 * h;
-    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288);
+    const unsigned e0 = 32u * c + 16u * h;
+    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288) + e0 * BITS / 8;
 #pragma unroll
-    for (int a = 0; a < 12; ++a)
-        quant16_store<BITS>(out + (a * 1024 + e0) * BITS / 8, u[a], cr, nrm, s, fast);
+    for (int a = 0; a < 12; ++a) quant16_store<BITS>(out + a * (1024 * BITS / 8), u[a], cr, nrm, s, fast);
     if (WRITE_ROT) {
         float* yr = X_rot + row * 12288 + e0;
 #pragma unroll
