@@ -363,6 +363,50 @@ def test_down_chain_end_to_end_sampled():
     assert_y_close(_host(Y)[rows][:, cols], y_o, flip_rows=fr, flip_cols=fc)
 
 
+@pytest.fixture(scope="module")
+def chain_m8192():
+    return synth.chain_config()
+
+
+@pytest.mark.parametrize("layer", ["qkv", "o", "gate_up", "down"])
+def test_decoder_chain_m8192_sampled(layer, chain_m8192):
+    """The decoder-layer chain at prefill size (M = 8192), each linear at its
+    full shape: activation quantization (FWHT-12288 for down, quant-only for
+    the others, whose inputs are already in the rotated basis), the weight fold
+    (R1 Haar 4096, head-wise R2 Haar 128, H_12288) and the GEMM.  Codes and
+    scales bit-exact with the oracle quantizer on the GPU's own rotated values
+    for sampled rows, accumulators bit-exact with the oracle's int64 GEMM on
+    the GPU's codes, and Y end to end against the oracle chain on sampled rows
+    and columns."""
+    L = chain_m8192[layer]
+    x, w, r, r_block, had_n = L["x"], L["w"], L["r"], L["r_block"], L["had_n"]
+    M, N = x.shape[0], w.shape[1]
+    rows = np.array([0, 1, 4097, M - 1])
+    cols = np.arange(0, N, N // 64)
+    Xq, xs, Xr = spin.spin_fwht_quant(_dev(x), had_n, want_rot=True)
+    _, Wq, ws = spin.spin_fold_rotation(_dev(w), None if r is None else _dev(r), r_block)
+    Y, acc = spin.spin_w4a4_gemm(Xq, xs, Wq, ws, want_acc=True)
+    sel = torch.from_numpy(rows).to(DEV)
+    xq_s, xs_s, xr_s = _host(Xq[sel]), _host(xs[sel]), _host(Xr[sel])
+    y_s, a_s = _host(Y[sel]), _host(acc[sel])
+    c_ref, s_ref = oracle.quantize_rows(xr_s)
+    assert np.array_equal(xs_s, s_ref) and np.array_equal(xq_s, oracle.pack_int4(c_ref))
+    qx = oracle.unpack_int4(xq_s)
+    qw = oracle.unpack_int4(_host(Wq))
+    a_ref = oracle.gemm_rows(qx, qw, np.arange(len(rows)))
+    assert np.array_equal(a_s.astype(np.int64), a_ref)
+    assert np.array_equal(y_s, oracle.dequant(a_ref, xs_s, _host(ws)))
+    # end to end against the oracle's own chain on sampled rows and columns
+    pk, s_o, y_rot = oracle.fwht_quant(x[rows], had_n)
+    assert_rows_close(xr_s, y_rot)
+    _, wq_o, ws_o = oracle.fold_rotation(w[:, cols], r, r_block)
+    a_o = oracle.gemm_rows(oracle.unpack_int4(pk), oracle.unpack_int4(wq_o), np.arange(len(rows)))
+    y_o = oracle.dequant(a_o, s_o, ws_o)
+    fr = code_flips(xq_s, pk, axis=1)
+    fc = code_flips(_host(Wq)[cols], wq_o, axis=1)
+    assert_y_close(y_s[:, cols], y_o, flip_rows=fr, flip_cols=fc)
+
+
 def test_repeat_runs_are_deterministic():
     cfg = synth.down_config(M=256)
     X = _dev(cfg["x"])
