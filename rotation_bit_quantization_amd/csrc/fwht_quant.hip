@@ -424,6 +424,149 @@ __global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
 }
 
 // ---------------------------------------------------------------------------
+// fwht_quant_k12288_wg: the same transform for a few rows (decode batches),
+// where one wave per row leaves most of the chip idle and a row's latency is
+// the kernel's time.  Four waves share a row: wave w runs the two matrix-core
+// stages of blocks 3w .. 3w + 2 exactly as fwht_quant_k12288_mfma does, the
+// stage-2 results go through 48 KB of LDS, and each thread then takes four
+// consecutive elements of every block (element e0 .. e0 + 3 of the block, the
+// registers r0 .. r0 + 3 of stage lane L) for the H12 mix, the absmax and the
+// quantizer.  Every value goes through the same operations as in the one-wave
+// kernel, so the two produce the same bits.
+
+// Four consecutive codes (2 bytes of nibbles, or 4 bytes) from the
+// magic-number quantizer, exact quotient near a tie or outside the fast range.
+template <int BITS>
+__device__ __forceinline__ void quant4_store(uint8_t* p, const float (&u)[4], float cr, float nrm, float s,
+                                             bool fast) {
+    uint32_t w = 0;
+    bool exact = !fast;
+    if (fast) {
+        uint32_t f[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, BITS == 4 ? kQuantMagic : kQuant8Magic));
+        if (BITS == 4) {
+            w = ((f[0] >> 16) & 0xFu) | ((f[1] >> 12) & 0xF0u) | ((f[2] >> 8) & 0xF00u) | ((f[3] >> 4) & 0xF000u);
+            exact = near_tie(f[0]) | near_tie(f[1]) | near_tie(f[2]) | near_tie(f[3]);
+        } else {
+            w = pack4_magic8(f);
+            exact = near_tie8(f[0]) | near_tie8(f[1]) | near_tie8(f[2]) | near_tie8(f[3]);
+        }
+    }
+    if (exact) {
+        int c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = BITS == 4 ? quant_exact(u[k] * nrm, s) : quant_exact8(u[k] * nrm, s);
+        w = BITS == 4 ? ((c[0] & 15) | ((c[1] & 15) << 4) | ((c[2] & 15) << 8) | ((c[3] & 15) << 12)) : pack4b(c);
+    }
+    if (BITS == 4)
+        *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(w);
+    else
+        *reinterpret_cast<uint32_t*>(p) = w;
+}
+
+constexpr int kWgRowThreads = 256;
+// Up to this many rows the four-waves-per-row kernel is the faster one (measured:
+// 5.6 against 8.7 us at 16 rows, 7.5 against 10.5 us at 512, 13.2 against
+// 12.7 us at 1024).
+constexpr int kWgMaxRows = 512;
+
+template <int BITS, bool WRITE_ROT>
+__global__ __launch_bounds__(kWgRowThreads) void fwht_quant_k12288_wg(
+    const __half* __restrict__ X, float norm, float mone, uint8_t* __restrict__ Xq,
+    float* __restrict__ x_scale, float* __restrict__ X_rot) {
+    __shared__ __attribute__((aligned(16))) float ex[12 * 64 * 16];   // [block][stage lane][register]
+    __shared__ float red[4];
+    __shared__ uint32_t redb[4];
+    const int t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const size_t row = blockIdx.x;
+    const __half* xr = X + row * 12288 + 32 * (lane & 31) + 16 * (lane >> 5);
+
+    u4v raw[3][2];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {  // read once: non-temporal
+        raw[j][0] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + (3 * wave + j) * 1024));
+        raw[j][1] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(xr + (3 * wave + j) * 1024 + 8));
+    }
+    u4v sa, sb;
+    operand_signs(lane, sa, sb);
+
+    // this thread's elements after the exchange
+    const int L = (t >> 1) & 63, r0 = 8 * (t >> 7) + 4 * (t & 1);
+    float nrm = norm * 32.0f;
+    unsigned magpair = 0x28002800u;     // +-2^-5
+    float y[12][4];
+    float amax = 0.0f;
+    for (int pass = 0; pass < 2; ++pass) {
+        const h8v b1a = __builtin_bit_cast(h8v, sa | magpair), b1b = __builtin_bit_cast(h8v, sb | magpair);
+        const h8v b2a = __builtin_bit_cast(h8v, sa | 0x3C003C00u), b2b = __builtin_bit_cast(h8v, sb | 0x3C003C00u);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const f16v u = hadamard1024_mfma(raw[j][0], raw[j][1], b1a, b1b, b2a, b2b, mone);
+            float4* dst = reinterpret_cast<float4*>(ex + ((3 * wave + j) * 64 + lane) * 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = make_float4(u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < 12; ++a) {
+            const float4 v = *reinterpret_cast<const float4*>(ex + (a * 64 + L) * 16 + r0);
+            y[a][0] = v.x; y[a][1] = v.y; y[a][2] = v.z; y[a][3] = v.w;
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float col12[12];
+#pragma unroll
+            for (int a = 0; a < 12; ++a) col12[a] = y[a][i];
+            h12_row(col12);
+#pragma unroll
+            for (int a = 0; a < 12; ++a) {
+                y[a][i] = col12[a];
+                mx = __builtin_fmaxf(mx, __builtin_fabsf(col12[a]));
+            }
+        }
+        amax = block_max_256(mx, red) * nrm;       // = max_i fl32(|u_i| * nrm); ends with a barrier
+        if (amax >= 2.0f || pass == 1) break;
+        // small (or all-zero) row: rescale stage 1 from the exact largest |x|
+        uint32_t mb = 0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                mb = max(mb, max(raw[j][0][k] & 0x7FFFu, (raw[j][0][k] >> 16) & 0x7FFFu));
+                mb = max(mb, max(raw[j][1][k] & 0x7FFFu, (raw[j][1][k] >> 16) & 0x7FFFu));
+            }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), o, 64)));
+        if (lane == 0) redb[wave] = mb;
+        __syncthreads();
+        mb = max(max(redb[0], redb[1]), max(redb[2], redb[3]));
+        const int m = min(20, 29 - static_cast<int>(mb >> 10));   // m >= -2 for any fp16 row
+        nrm = __builtin_ldexpf(norm, 5 - m);
+        magpair = __builtin_bit_cast(unsigned short, static_cast<_Float16>(__builtin_ldexpf(1.0f, m - 5))) * 0x10001u;
+    }
+
+    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
+    if (t == 0) x_scale[row] = s;
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    const float cr = fast ? nrm * __fdiv_rn(1.0f, s) : 0.0f;
+    const unsigned e0 = 32u * (L & 31) + 16u * (L >> 5) + r0;
+    uint8_t* out = Xq + row * (BITS == 4 ? 6144 : 12288) + e0 * BITS / 8;
+#pragma unroll
+    for (int a = 0; a < 12; ++a) quant4_store<BITS>(out + a * (1024 * BITS / 8), y[a], cr, nrm, s, fast);
+    if (WRITE_ROT) {
+        float* yr = X_rot + row * 12288 + e0;
+#pragma unroll
+        for (int a = 0; a < 12; ++a)
+            *reinterpret_cast<float4*>(yr + a * 1024) =
+                make_float4(y[a][0] * nrm, y[a][1] * nrm, y[a][2] * nrm, y[a][3] * nrm);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // quant_rows: had_n = 1 (the rows are already in the rotated basis, e.g. R1
 // folded upstream): per-token quantization only.  One workgroup of 256
 // threads per row; thread t holds the chunks of 8 consecutive values t,
@@ -525,6 +668,15 @@ hipError_t launch_fwht_quant_bits(const void* X, bool x_f16, int M, int K, HadOr
     if (x_f16 && h.n == 12288 && K == 12288) {
         const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
         const __half* x = static_cast<const __half*>(X);
+        if (M <= kWgMaxRows) {
+            if (X_rot)
+                hipLaunchKernelGGL((fwht_quant_k12288_wg<BITS, true>), dim3(M), dim3(kWgRowThreads), 0, s, x, norm,
+                                   -1.0f, Xq, x_scale, X_rot);
+            else
+                hipLaunchKernelGGL((fwht_quant_k12288_wg<BITS, false>), dim3(M), dim3(kWgRowThreads), 0, s, x, norm,
+                                   -1.0f, Xq, x_scale, X_rot);
+            return hipGetLastError();
+        }
         if (X_rot)
             hipLaunchKernelGGL((fwht_quant_k12288_mfma<BITS, true>), dim3(M), dim3(64), 0, s, x, norm, -1.0f, Xq,
                                x_scale, X_rot);

@@ -158,6 +158,31 @@ def test_fwht_quant_12288_magnitude_range():
     assert ((s > 0) == (np.abs(x.astype(np.float32)).max(axis=1) > 0)).all()
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_fwht_quant_12288_both_kernels_agree(bits):
+    """Batches of up to 512 rows of 12288 run four waves per row, larger ones
+    one wave per row; both must give the same bits.  The magnitude rows (both
+    passes of the matrix-core path) lead a batch of 619 rows, checked against
+    the oracle, and its first 200 rows are run again as a small batch."""
+    rng = np.random.default_rng(12)
+    extra, _ = synth.outlier_activations(rng, 600, 12288, 12, 100.0)
+    lead = magnitude_rows()
+    x = np.concatenate([lead, extra]).astype(np.float16)
+    assert x.shape[0] > 512 >= 200
+    if bits == 4:
+        xq, s, xr = check_fwht_quant(x, 12288, rows=np.r_[0:len(lead), 100, x.shape[0] - 1])
+        run = lambda a: spin.spin_fwht_quant(_dev(a), 12288, want_rot=True)
+    else:
+        run = lambda a: spin.spin_fwht_quant8(_dev(a), 12288, want_rot=True)
+        xq, s, xr = (_host(v) for v in run(x))
+        c_ref, s_ref = oracle.quantize_rows(xr, 127)
+        assert np.array_equal(xq, c_ref) and np.array_equal(s, s_ref)
+    xq2, s2, xr2 = (_host(v) for v in run(x[:200]))
+    assert np.array_equal(xr2.view(np.uint32), xr[:200].view(np.uint32))
+    assert np.array_equal(s2.view(np.uint32), s[:200].view(np.uint32))
+    assert np.array_equal(xq2, xq[:200])
+
+
 def test_fwht_quant_down_config_full_size():
     cfg = synth.down_config()
     rows = np.array([0, 1, 511, 2048, 4095])
