@@ -260,16 +260,15 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 
 // ---------------------------------------------------------------------------
 // w4a4_gemm_m16: decode-sized M <= 16, where the product is bound by reading
-// the weights once.  One workgroup per 16 output columns; its 8 waves split K
-// into 8 ranges of 128-code chunks, each wave runs two 16x16x64 int8 MFMA
-// chains over its range (lane l: row / column l % 16, 16 bytes at offset
-// 16 (l / 16) of each 64-byte chunk, the MFMA pair taking bytes 0-7 then
-// 8-15, identically for both operands), and the eight partial accumulators
-// are added exactly in LDS.  Rows beyond M and columns beyond N read row 0 /
-// the last column (valid memory) and are never stored.
-constexpr int kDecodeWaves = 8;
-
-template <bool WRITE_ACC>
+// the weights once.  One workgroup per 16 output columns; its waves (8, or 2
+// when there are enough column groups to fill the chip) split K into ranges
+// of 128-code chunks, each wave runs two 16x16x64 int8 MFMA chains over its
+// range (lane l: row / column l % 16, 16 bytes at offset 16 (l / 16) of each
+// 64-byte chunk, the MFMA pair taking bytes 0-7 then 8-15, identically for
+// both operands), and the partial accumulators are added exactly in LDS.
+// Rows beyond M and columns beyond N read the last row / column (valid
+// memory) and are never stored.
+template <bool WRITE_ACC, int kDecodeWaves>
 __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
     const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
@@ -283,6 +282,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
     const size_t rowBytes = static_cast<size_t>(K) / 2;
     const uint8_t* pa = Xq + static_cast<size_t>(ra) * rowBytes + 16 * (lane >> 4);
     const uint8_t* pb = Wq + static_cast<size_t>(cb) * rowBytes + 16 * (lane >> 4);
+    // the epilogue's scales, requested before the operands so that their
+    // latency hides behind the main loads
+    const int col = n0 + (lane & 15);
+    const float sw = w_scale[cb];
+    float sx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sx[r] = x_scale[min((lane >> 4) * 4 + r, M - 1)];
     const int chunks = K / 128;
     const int beg = (chunks * wave) / kDecodeWaves, end = (chunks * (wave + 1)) / kDecodeWaves;
     v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
@@ -301,15 +307,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
     v4i sum = part[0][lane];
 #pragma unroll
     for (int w = 1; w < kDecodeWaves; ++w) sum += part[w][lane];
-    const int col = n0 + (lane & 15);
     if (col >= N) return;
-    const float sw = w_scale[col];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = (lane >> 4) * 4 + r;
         if (row < M) {
             const int a = sum[r] >> 8;
-            float y = static_cast<float>(a) * x_scale[row];
+            float y = static_cast<float>(a) * sx[r];
             y = y * sw;
             Y[static_cast<size_t>(row) * N + col] = y;
             if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
@@ -324,12 +328,28 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
                             int32_t* acc_out, hipStream_t s) {
     if (M <= 16 && K % 128 == 0) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
-        if (acc_out)
-            hipLaunchKernelGGL((w4a4_gemm_m16<true>), grid, dim3(64 * kDecodeWaves), 0, s, Xq,
-                               x_scale, Wq, w_scale, M, N, K, Y, acc_out);
-        else
-            hipLaunchKernelGGL((w4a4_gemm_m16<false>), grid, dim3(64 * kDecodeWaves), 0, s, Xq,
-                               x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+        // many column groups (gate/up): two waves each, so that every wave
+        // streams a longer K range; few (qkv, o_proj, down): eight waves
+        int cus = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        const bool wide = cus > 0 && static_cast<long long>(grid.x) >= 4LL * cus;
+        if (wide) {
+            if (acc_out)
+                hipLaunchKernelGGL((w4a4_gemm_m16<true, 2>), grid, dim3(128), 0, s, Xq, x_scale, Wq, w_scale, M, N,
+                                   K, Y, acc_out);
+            else
+                hipLaunchKernelGGL((w4a4_gemm_m16<false, 2>), grid, dim3(128), 0, s, Xq, x_scale, Wq, w_scale, M,
+                                   N, K, Y, acc_out);
+        } else {
+            if (acc_out)
+                hipLaunchKernelGGL((w4a4_gemm_m16<true, 8>), grid, dim3(512), 0, s, Xq, x_scale, Wq, w_scale, M, N,
+                                   K, Y, acc_out);
+            else
+                hipLaunchKernelGGL((w4a4_gemm_m16<false, 8>), grid, dim3(512), 0, s, Xq, x_scale, Wq, w_scale, M,
+                                   N, K, Y, acc_out);
+        }
         return hipGetLastError();
     }
     if (K % kStepCodes == 0) {
