@@ -56,11 +56,11 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
     "fwht_quant": {"sources": {"fwht_quant.hip": "0be8bc922ec664bc", "spin_device.h": "c63f8fbd91ccf2df"},
-                  "read": 101782769, "write": 25297021},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "3a7b38b8282c9e01", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "c63f8fbd91ccf2df"},
-                 "read": 151261917, "write": 67108864},
+                  "read": 101755642, "write": 25297099},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "d00bf9c0b6026fbd", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "c63f8fbd91ccf2df"},
+                 "read": 151261900, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "51391dd2ab5b766c", "spin_device.h": "c63f8fbd91ccf2df"},
-                "read": 33646468, "write": 8650752},
+                "read": 33646488, "write": 8650752},
 }
 
 

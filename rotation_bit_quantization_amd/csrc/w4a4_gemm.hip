@@ -259,6 +259,154 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 }
 
 // ---------------------------------------------------------------------------
+// w4a4_gemm_wide: 256 x 384 output tiles for shapes whose 256 x 256 tiles
+// would leave the last round of workgroups part-empty (qkv_proj, N = 6144:
+// 384 tiles of 256 x 256 on 256 CUs, 256 of 256 x 384).  Eight waves (two per
+// SIMD), each 128 x 96 as 4 x 3 tiles of the 32x32x32 int8 MFMA; the same
+// widening, LDS-DMA operand pipeline (three 40 KB stages, two steps ahead),
+// slot swizzle, fragment layout and epilogue as w4a4_gemm_256.  A stage holds
+// A's 8 and then B's 12 blocks of 32 rows; each wave issues five of its forty
+// 1 KB DMA instructions (instruction q fills half q % 2 of block q / 2), from
+// the block's wave-uniform row base plus the lane's offset in the block.  Only
+// launched for whole tiles (M % 256 == 0, N % 384 == 0).
+constexpr int kWTM = 256;
+constexpr int kWTN = 384;
+constexpr int kWStageBytes = (kWTM + kWTN) * kStepBytes;
+constexpr int kWStages = 3;
+constexpr int kWThreads = 512;
+constexpr int kWDma = (kWTM + kWTN) * kStepBytes / 1024 / (kWThreads / 64);
+static_assert(kWDma * 1024 * (kWThreads / 64) == kWStageBytes, "DMA instructions must tile a stage");
+
+// 16 bytes per lane from sbase + voff into LDS at lds_base + 16 * lane, with
+// a wave-uniform 64-bit base in scalar registers and a 32-bit per-lane offset
+// (the same M0 handling as lds_dma16).
+__device__ __forceinline__ void lds_dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+        : "memory");
+}
+
+template <bool WRITE_ACC>
+__global__ __launch_bounds__(kWThreads) void w4a4_gemm_wide(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kWStages * kWStageBytes];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    int tm, tn;
+    tile_of(blockIdx.x, (M + kWTM - 1) / kWTM, (N + kWTN - 1) / kWTN, &tm, &tn);
+    const int m0 = tm * kWTM, n0 = tn * kWTN;
+    const int wm = (wave >> 2) * 128, wn = (wave & 3) * 96;
+    const size_t rowBytes = static_cast<size_t>(K) / 2;
+    const int steps = K / kStepCodes;
+
+    // a lane's byte offset inside a 32-row block for each half (the row and
+    // its swizzled 16-byte slot); the block's row base is wave-uniform and
+    // goes in as the scalar base of the load
+    uint32_t voff[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int r = 16 * half + (lane >> 2);
+        voff[half] = static_cast<uint32_t>(r * rowBytes + ((lane & 3) ^ slot_swz(r)) * 16);
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    auto issue = [&](int step) {
+        const uint32_t stage = lds0 + (step % kWStages) * kWStageBytes;
+        const size_t off = static_cast<size_t>(step) * kStepBytes;
+#pragma unroll
+        for (int k = 0; k < kWDma; ++k) {
+            const int q = __builtin_amdgcn_readfirstlane(kWDma * wave + k);
+            const int blk = q >> 1, half = q & 1;
+            const uint8_t* base = blk < kWTM / 32 ? Xq + static_cast<size_t>(m0 + 32 * blk) * rowBytes
+                                                  : Wq + static_cast<size_t>(n0 + 32 * (blk - kWTM / 32)) * rowBytes;
+            lds_dma16_s(voff[half], base + off, stage + blk * 2048 + half * 1024);
+        }
+    };
+
+    v16i acc[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int fr = lane & 31;
+    const int h0 = 2 * (lane >> 5);
+    const int fo0 = fr * kStepBytes + ((h0 ^ slot_swz(fr)) << 4);
+    const int fo1 = fr * kStepBytes + (((h0 + 1) ^ slot_swz(fr)) << 4);
+
+#pragma unroll
+    for (int s = 0; s < kWStages - 1; ++s)
+        if (s < steps) issue(s);
+
+    for (int step = 0; step < steps; ++step) {
+        // this wave's loads of `step` are done once at most those of the one
+        // later step in flight remain; the barrier then also guarantees that
+        // every wave has finished reading the stage refilled below
+        if (step + 1 < steps) SPIN_WAIT_VMCNT(kWDma);
+        else SPIN_WAIT_VMCNT(0);
+        barrier_no_fence();
+        if (step + kWStages - 1 < steps) issue(step + kWStages - 1);
+        const uint8_t* st = lds + (step % kWStages) * kWStageBytes;
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const int fo = part ? fo1 : fo0;
+            uint4 qa[4], qb[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                qb[j] = *reinterpret_cast<const uint4*>(st + kWTM * kStepBytes + (wn + j * 32) * kStepBytes + fo);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qa[i] = *reinterpret_cast<const uint4*>(st + (wm + i * 32) * kStepBytes + fo);
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                v4i fb[3];
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    fb[j] = widen16(sub ? make_uint2(qb[j].z, qb[j].w) : make_uint2(qb[j].x, qb[j].y));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4i fa = widen16(sub ? make_uint2(qa[i].z, qa[i].w) : make_uint2(qa[i].x, qa[i].y));
+#pragma unroll
+                    for (int j = 0; j < 3; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row >= M) continue;
+            const float sx = x_scale[row];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int col = n0 + wn + j * 32 + (lane & 31);
+                if (col < N) {
+                    const int a = acc[i][j][r] >> 8;
+                    float y = static_cast<float>(a) * sx;
+                    y = y * w_scale[col];
+                    Y[static_cast<size_t>(row) * N + col] = y;
+                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // w4a4_gemm_m16: decode-sized M <= 16, where the product is bound by reading
 // the weights once.  One workgroup per 16 output columns; its waves (8, or 2
 // when there are enough column groups to fill the chip) split K into ranges
@@ -354,6 +502,25 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
     }
     if (K % kStepCodes == 0) {
         const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
+        {
+            // 256 x 384 tiles where they fill the last round of workgroups
+            // better (qkv_proj: 256 instead of 384 tiles on 256 CUs)
+            int cus = 0, dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                cus = 0;
+            const long long wide = static_cast<long long>(N / kWTN) * (M / kWTM);
+            auto fill = [&](long long t) { return static_cast<double>(t) / (((t + cus - 1) / cus) * cus); };
+            if (cus > 0 && N % kWTN == 0 && M % kWTM == 0 && fill(wide) > fill(tiles) + 0.05) {
+                if (acc_out)
+                    hipLaunchKernelGGL((w4a4_gemm_wide<true>), dim3(static_cast<unsigned>(wide)), dim3(kWThreads), 0,
+                                       s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+                else
+                    hipLaunchKernelGGL((w4a4_gemm_wide<false>), dim3(static_cast<unsigned>(wide)), dim3(kWThreads), 0,
+                                       s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+                return hipGetLastError();
+            }
+        }
         dim3 grid(static_cast<unsigned>(tiles));
         if (acc_out)
             hipLaunchKernelGGL((w4a4_gemm_256<true>), grid, dim3(kGemmThreads), 0, s, Xq, x_scale,

@@ -310,6 +310,20 @@ def test_gemm_decode_sizes(M, N, K):
     check_gemm(qx, qw, sx, sw)
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 4096])
+def test_gemm_qkv_shape_wide_tiles(K):
+    """M = 4096, N = 6144 (qkv_proj) runs 256 x 384 tiles: one step (shorter
+    than the load pipeline), two, three and the full K = 4096; sampled rows
+    from every row block, all columns."""
+    rng = np.random.default_rng(K + 5)
+    M, N = 4096, 6144
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw, rows=[0, 1, 127, 255, 256, 2047, 3969, 4095])
+
+
 def test_gemm_extreme_accumulators():
     K = 12288
     qx = np.full((3, K), 7, np.int8)
