@@ -16,7 +16,8 @@
 // fwht_quant_k12288_mfma: fp16 rows of 12288 with had_n = 12288 (the R4 /
 // down_proj case), one wave per row, the two 32-point stages of each
 // 1024-block on the matrix cores and the order-12 mix in registers (see the
-// kernel).
+// kernel).  fwht_quant_k12288_wg: the same arithmetic with four waves per
+// row, for batches of up to kWgMaxRows rows (decode), bit-identical.
 #include "spin_device.h"
 #include "spin_internal.h"
 

@@ -11,6 +11,11 @@
 // times the true dot product (exact while 49 * K * 256 < 2^31); an arithmetic
 // shift by 8 recovers it exactly.  The k order inside a 64-wide MFMA step is
 // permuted identically on both sides, which leaves the dot product unchanged.
+//
+// Kernels: w4a4_gemm_256 (256 x 256 tiles, the general case), w4a4_gemm_wide
+// (256 x 384 tiles where they fill the last round of workgroups better),
+// w4a4_gemm_m16 (M <= 16, weight-streaming) and w4a4_gemm_basic (K not a
+// multiple of 128).
 #include "gemm_common.h"
 #include "spin_device.h"
 #include "spin_internal.h"
