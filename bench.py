@@ -329,7 +329,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              f"(the path shards by tokens with no communication; see DESIGN.md)", file=sys.stderr)
+              f"(fwht_quant and kv_quant shard by tokens with no communication; the GEMM shards by output "
+              f"columns, or by K with an exact int32 all-reduce before the epilogue)", file=sys.stderr)
         sys.exit(2)
 
     import torch
