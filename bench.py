@@ -34,13 +34,13 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
 M, K, N, HAD_N = 4096, 12288, 4096, 12288
 FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
-# The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2187.2
+# The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2180.2
 # VALU instructions, 72 of them MFMA (rocprofv3 SQ_INSTS_VALU and
-# SQ_INSTS_MFMA over SQ_WAVES on the down_proj workload), so 2115.2 vector
+# SQ_INSTS_MFMA over SQ_WAVES on the down_proj workload), so 2108.2 vector
 # lane-operations per lane for its 192 elements (the hi/lo split, the
-# 50-operation H12, absmax, quantize and pack): 11.02 per element, against
+# 50-operation H12, absmax, quantize and pack): 10.98 per element, against
 # the chip's 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations per second.
-FWHT_VALU_OPS_PER_ELEMENT = (8958848.0 - 294912.0) / 4096.0 / 192.0
+FWHT_VALU_OPS_PER_ELEMENT = (8930176.0 - 294912.0) / 4096.0 / 192.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 KV_T, KV_H, KV_D = 4096, 32, 128
 KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
@@ -55,12 +55,12 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "0be8bc922ec664bc", "spin_device.h": "c63f8fbd91ccf2df"},
-                  "read": 101755642, "write": 25297099},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "d00bf9c0b6026fbd", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "c63f8fbd91ccf2df"},
-                 "read": 151261900, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "51391dd2ab5b766c", "spin_device.h": "c63f8fbd91ccf2df"},
-                "read": 33646488, "write": 8650752},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "0be8bc922ec664bc", "spin_device.h": "bbe2e2331921046d"},
+                  "read": 101805533, "write": 25297045},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "d00bf9c0b6026fbd", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "bbe2e2331921046d"},
+                 "read": 151262079, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "68f3dc301d7673ca", "spin_device.h": "bbe2e2331921046d"},
+                "read": 33636265, "write": 8650752},
 }
 
 

@@ -46,11 +46,12 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
 // Quantize eight held values z (true value = sign * z * norm) of one vector
 // whose fp16 scale is s16: returns one dword of codes.  Fast path when s16 is
 // a normal fp16 (then |y / s16| < 7.5 so no clamp is needed and the
-// magic-number estimate plus exact near-tie fallback applies); otherwise the
+// magic-number estimate plus exact near-tie fallback applies; 1/s16 from
+// v_rcp_f32 keeps the estimate well inside the fallback window); otherwise the
 // exact quotient and clamp.
 __device__ __forceinline__ uint32_t kv_codes(const float* z, float sign, float norm, float sf) {
     if (sf >= 0x1p-14f && sf <= 65504.0f) {
-        const float cr = sign * (norm * __fdiv_rn(1.0f, sf));
+        const float cr = sign * (norm * __builtin_amdgcn_rcpf(sf));
         uint32_t f[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], cr, kQuantMagic));
@@ -73,7 +74,7 @@ __device__ __forceinline__ uint32_t kv_codes(const float* z, float sign, float n
 // The 8-bit variant of kv_codes: two dwords of byte codes.
 __device__ __forceinline__ uint2 kv_codes8(const float* z, float sign, float norm, float sf) {
     if (sf >= 0x1p-14f && sf <= 65504.0f) {
-        const float cr = sign * (norm * __fdiv_rn(1.0f, sf));
+        const float cr = sign * (norm * __builtin_amdgcn_rcpf(sf));
         uint32_t f[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = __float_as_uint(__builtin_fmaf(z[k], cr, kQuant8Magic));
@@ -174,7 +175,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
 #pragma unroll
             for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[p][k]));
             mx = row16_max(mx) * nrm;                 // = max_i fl32(|z_i| * norm)
-            const __half s16 = __float2half_rn(__fdiv_rn(mx, BITS == 4 ? kSeven : kQmax8));
+            const __half s16 = __float2half_rn(BITS == 4 ? div_by_qmax(mx, kSeven, kRcpSeven)
+                                                          : div_by_qmax(mx, kQmax8, kRcpQmax8));
             const float sf = __half2float(s16);
             if (BITS == 4)
                 reinterpret_cast<uint32_t*>(codes)[g * 16 + l] = kv_codes(v[p], sign, nrm, sf);

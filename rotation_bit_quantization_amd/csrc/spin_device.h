@@ -34,6 +34,26 @@ __device__ __forceinline__ int quant_exact8(float y, float s) {
     return static_cast<int>(q);
 }
 
+// fl32(a / d) for d = 7 or 127 without a division instruction sequence:
+// q = fl32(a * rd) with rd = fl32(1 / d), the remainder a - d * q is exact in
+// one FMA, and q + remainder * rd is rounded once more.  For these two
+// divisors the result is the IEEE quotient for every a whose quotient is a
+// normal float32 (checked over all 2^23 significands; every step scales
+// exactly with a power of two).  A subnormal quotient lies far below the
+// smallest fp16 scale, where both values convert to the same fp16 zero.  The
+// empty asm keeps the float32 result: without it the compiler may fuse the
+// last FMA into a following fp16 conversion, which then rounds the exact sum
+// once instead of the float32 quotient.
+constexpr float kRcpSeven = 0x1.24924ap-3f;   // fl32(1 / 7)
+constexpr float kRcpQmax8 = 0x1.020408p-7f;   // fl32(1 / 127)
+__device__ __forceinline__ float div_by_qmax(float a, float d, float rd) {
+    const float q = __fmul_rn(a, rd);
+    const float r = __builtin_fmaf(-q, d, a);
+    float s = __builtin_fmaf(r, rd, q);
+    asm("" : "+v"(s));
+    return s;
+}
+
 // Four signed byte codes (c[0] lowest) -> one little-endian dword.
 __device__ __forceinline__ uint32_t pack4b(const int* c) {
     return (static_cast<uint32_t>(c[0]) & 0xFFu) | ((static_cast<uint32_t>(c[1]) & 0xFFu) << 8) |
@@ -91,13 +111,17 @@ __device__ __forceinline__ float hadamard_sign(unsigned i, unsigned j, int log2p
     return s;
 }
 
-// Max of a float over the 16 lanes of each DPP row (every lane gets it).
+// Max of a non-negative float over the 16 lanes of each DPP row (every lane
+// gets it).  For v >= 0 the float order is the unsigned order of the bit
+// patterns, so the reduction runs on the integers: no NaN canonicalisation
+// and each level is one v_max_u32 with the DPP operand folded in.
 __device__ __forceinline__ float row16_max(float v) {
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false))); // lane ^ 7
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false))); // lane ^ 15
-    return v;
+    unsigned u = __float_as_uint(v);
+    u = max(u, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0xB1, 0xF, 0xF, true)));   // lane ^ 1
+    u = max(u, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x4E, 0xF, 0xF, true)));   // lane ^ 2
+    u = max(u, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x141, 0xF, 0xF, true)));  // lane ^ 7
+    u = max(u, static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x140, 0xF, 0xF, true)));  // lane ^ 15
+    return __uint_as_float(u);
 }
 
 // Block-wide max of non-negative floats over 256 threads (4 waves).  `red`
@@ -232,7 +256,8 @@ __device__ __forceinline__ void dpp_wht16(float* r, float s1, float s2, float s3
 }
 
 // Fast quantizer for a row whose scale s is in the normal range.  With
-// cr = fl32(norm / s) (signed per element as needed) the fused
+// cr = norm / s to within two float32 roundings (or three where 1/s comes
+// from v_rcp_f32, accurate to one ulp), signed per element as needed, the fused
 // f = fma(z, cr, kQuantMagic) lands y/s + 1/2 on a grid of 2^-16 in the low
 // mantissa bits: bits 16..19 hold the nibble of floor(y/s + 1/2) and bits
 // 0..15 the fraction, offset by one unit so that an exact tie reads 1.
@@ -247,9 +272,10 @@ __device__ __forceinline__ bool near_tie(uint32_t fbits) { return (fbits & 0xFFF
 // 8-bit codes: f = fma(z, cr, kQuant8Magic) lands y/s + 1/2 on a grid of 2^-14
 // (f in [512, 1024) for |y/s| <= 127.5): bits 14..21 hold the two's-complement
 // byte of floor(y/s + 1/2), bits 0..13 the fraction, offset by two units so
-// that an exact tie reads 2.  The estimate of y/s is within ~0.7 units of
-// fl32(y / s) at |y/s| <= 127.5 (five float32 roundings of relative size 2^-24
-// at magnitude < 2^7), plus half a unit from rounding f itself; a fraction
+// that an exact tie reads 2.  The estimate of y/s is within ~0.8 units of
+// fl32(y / s) at |y/s| <= 127.5 (float32 roundings of relative size 2^-24 at
+// magnitude < 2^7, and 2^-23 where 1/s comes from v_rcp_f32, which is
+// accurate to one ulp), plus half a unit from rounding f itself; a fraction
 // below 5 units (two below a tie to three above) sends the code to the exact
 // IEEE quotient.
 constexpr float kQuant8Magic = 768.5f + 0x1p-13f;
