@@ -14,6 +14,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import scipy.linalg
 import pytest
 
 import oracle
@@ -205,3 +206,76 @@ def test_kurtosis_falls_to_about_three_after_rotation():
     xs[:, :2] *= 100.0
     assert oracle.mean_kurtosis(xs) >= 50
     assert 2.7 <= oracle.mean_kurtosis(xs @ r.astype(np.float64)) <= 3.3
+
+
+def _per_head_kurtosis(x):
+    """Mean Pearson kurtosis across the 128 dims of each (token, head), per head."""
+    T, H, D = x.shape
+    return np.array([oracle.mean_kurtosis(np.asarray(x[:, h], np.float64), max_tokens=T) for h in range(H)])
+
+
+@pytest.mark.parametrize("fn", ["kv_quant", "kv_quant8"])
+def test_kv_rotate_branch_is_head_wise_h128(fn):
+    """R3 is an online Hadamard of order 128 applied to every (token, head)
+    vector (page "SpinQuant, Reproduced", Q5).  Pinned two ways that share no
+    code with the oracle: scipy's Sylvester matrix on fp16 inputs, and the
+    textbook butterfly on integer inputs (exact before the 1/sqrt(128))."""
+    kv = getattr(oracle, fn)
+    cfg = synth.kv_config(T=6, H=3)
+    x = cfg["k"]
+    _, _, y = kv(x, rotate=True)
+    h128 = scipy.linalg.hadamard(128).astype(np.float64) / np.sqrt(128.0)
+    ref = np.einsum("thd,de->the", x.astype(np.float64), h128).astype(np.float32)
+    assert y.dtype == np.float32 and y.shape == x.shape
+    # one float32 rounding of the same float64 sum: equal up to one ulp
+    assert np.all(np.abs(y - ref) <= np.spacing(np.abs(ref)))
+    # a vector that a missing rotation would leave unchanged is moved
+    assert not np.allclose(y, x.astype(np.float32))
+    xi = np.random.default_rng(11).integers(-60, 60, size=(2, 2, 128)).astype(np.float16)
+    _, _, yi = kv(xi, rotate=True)
+    bf = _textbook_fwht(xi.astype(np.int64)).astype(np.float64) / np.sqrt(128.0)
+    assert np.array_equal(yi, bf.astype(np.float32))
+
+
+@pytest.mark.parametrize("fn", ["kv_quant", "kv_quant8"])
+def test_kv_rotation_brings_per_head_kurtosis_to_about_three(fn):
+    """The KV recipe (2 outlier dims per head x30) has per-head kurtosis in
+    the tens or more before R3 and about 3 after (page "SpinQuant,
+    Reproduced", Q3: kurtosis falls to about 3 under rotation)."""
+    kv = getattr(oracle, fn)
+    x = synth.kv_config(T=256, H=4)["k"]
+    before = _per_head_kurtosis(x)
+    _, _, y = kv(x, rotate=True)
+    after = _per_head_kurtosis(y)
+    assert np.all(before >= 50), before
+    assert np.all((after >= 1.5) & (after <= 3.5)), after
+    # the V path (rotate=0) leaves the statistics as they are
+    _, _, yv = kv(x, rotate=False)
+    assert np.allclose(_per_head_kurtosis(yv), before)
+
+
+@pytest.mark.parametrize("eps", [1e-3, 0.25, 2.0])
+def test_orthogonality_error_known_defects(eps):
+    """max |R^T R - I| (page "SpinQuant, Reproduced", Q6) on matrices whose
+    defect has a closed form: diag(1, 1 + e) -> 2e + e^2; a rotation scaled by
+    c -> |c^2 - 1|; a shear [[1, e], [0, 1]] -> max(e, e^2)."""
+    d = np.diag([1.0, 1.0 + eps])
+    assert oracle.orthogonality_error(d) == pytest.approx(2 * eps + eps * eps, rel=1e-12)
+    th = 0.7
+    rot = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+    c = 1.0 + eps
+    assert oracle.orthogonality_error(c * rot) == pytest.approx(abs(c * c - 1.0), rel=1e-9)
+    shear = np.array([[1.0, eps], [0.0, 1.0]])
+    assert oracle.orthogonality_error(shear) == pytest.approx(max(eps, eps * eps), rel=1e-12)
+
+
+def test_orthogonality_error_of_exact_rotations_is_rounding_only():
+    """A normalised Hadamard and a float64 Haar draw are orthogonal to rounding;
+    the same matrices with one entry changed are not."""
+    h = scipy.linalg.hadamard(64) / 8.0
+    assert oracle.orthogonality_error(h) == 0.0
+    g = np.random.default_rng(5).standard_normal((32, 32))
+    q, _ = np.linalg.qr(g)
+    assert oracle.orthogonality_error(q) < 1e-14
+    q[3, 4] += 1e-3
+    assert oracle.orthogonality_error(q) > 1e-4
