@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "spin_internal.h"
@@ -34,6 +35,9 @@ bool parse_had(int n, spin::HadOrder* h) {
 }
 
 spin_status from_hip(hipError_t e) { return e == hipSuccess ? SPIN_OK : SPIN_ERR_HIP; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0: not queried yet
 
 // Shared by the 4-bit and 8-bit entry points; `bits` picks the code width.
 spin_status fwht_quant_impl(const void* X, spin_dtype x_dtype, int M, int K, int had_n, int bits,
@@ -69,6 +73,20 @@ spin_status kv_quant_impl(const void* X, spin_dtype x_dtype, int T, int H, int D
 }
 
 }  // namespace
+
+int spin::device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev >= kMaxDevices) {
+        int cus = 0;
+        return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? cus : 0;
+    }
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 extern "C" {
 

@@ -175,6 +175,10 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
 #pragma unroll
             for (int k = 0; k < 8; ++k) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[p][k]));
             mx = row16_max(mx) * nrm;                 // = max_i fl32(|z_i| * norm)
+            // Any absmax above 65504 * 7 rounds to an fp16 infinity; clamping
+            // at 2^100 keeps that result for an infinite absmax, whose
+            // remainder step in div_by_qmax would otherwise give NaN.
+            mx = __builtin_fminf(mx, 0x1p100f);
             const __half s16 = __float2half_rn(BITS == 4 ? div_by_qmax(mx, kSeven, kRcpSeven)
                                                           : div_by_qmax(mx, kQmax8, kRcpQmax8));
             const float sf = __half2float(s16);

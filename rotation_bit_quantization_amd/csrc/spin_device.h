@@ -43,7 +43,8 @@ __device__ __forceinline__ int quant_exact8(float y, float s) {
 // smallest fp16 scale, where both values convert to the same fp16 zero.  The
 // empty asm keeps the float32 result: without it the compiler may fuse the
 // last FMA into a following fp16 conversion, which then rounds the exact sum
-// once instead of the float32 quotient.
+// once instead of the float32 quotient.  a must be finite (an infinite a
+// gives NaN through the remainder).
 constexpr float kRcpSeven = 0x1.24924ap-3f;   // fl32(1 / 7)
 constexpr float kRcpQmax8 = 0x1.020408p-7f;   // fl32(1 / 127)
 __device__ __forceinline__ float div_by_qmax(float a, float d, float rd) {

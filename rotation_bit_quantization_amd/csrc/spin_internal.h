@@ -30,6 +30,10 @@ hipError_t launch_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, hipStream_t s);
 
+// Compute units of the current device, queried once per device and cached
+// (0 if the runtime cannot tell); safe to call from several threads.
+int device_cu_count();
+
 hipError_t launch_fold_rotation(const float* W, int K, int N, const float* R, int r_block,
                                 HadOrder h, float* W_rot, uint8_t* Wq, float* w_scale,
                                 hipStream_t s);

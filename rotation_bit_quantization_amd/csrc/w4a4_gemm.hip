@@ -483,10 +483,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         // many column groups (gate/up): two waves each, so that every wave
         // streams a longer K range; few (qkv, o_proj, down): eight waves
-        int cus = 0, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
+        const int cus = device_cu_count();
         const bool wide = cus > 0 && static_cast<long long>(grid.x) >= 4LL * cus;
         if (wide) {
             if (acc_out)
@@ -510,10 +507,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
         {
             // 256 x 384 tiles where they fill the last round of workgroups
             // better (qkv_proj: 256 instead of 384 tiles on 256 CUs)
-            int cus = 0, dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-                cus = 0;
+            const int cus = device_cu_count();
             const long long wide = static_cast<long long>(N / kWTN) * (M / kWTM);
             auto fill = [&](long long t) { return static_cast<double>(t) / (((t + cus - 1) / cus) * cus); };
             if (cus > 0 && N % kWTN == 0 && M % kWTM == 0 && fill(wide) > fill(tiles) + 0.05) {
