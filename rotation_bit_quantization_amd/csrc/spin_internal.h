@@ -25,6 +25,13 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
 hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, int bits,
                            uint8_t* codes, uint16_t* scale, float* X_rot, hipStream_t s);
 
+// The FP6 matrix-core path of launch_w4a4_gemm (exact for K <= kGemmFp6MaxK).
+constexpr int kGemmFp6MaxK = 65536;
+bool w4a4_gemm_fp6_applies(int M, int N, int K);
+hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                                const float* w_scale, int M, int N, int K, float* Y,
+                                int32_t* acc_out, hipStream_t s);
+
 // Int8 activation codes [M][K] against packed INT4 weights [N][K/2]; K % 128 == 0.
 hipError_t launch_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,

@@ -502,6 +502,8 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
         }
         return hipGetLastError();
     }
+    if (w4a4_gemm_fp6_applies(M, N, K))
+        return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
     if (K % kStepCodes == 0) {
         const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
         {

@@ -1,0 +1,60 @@
+"""GPU parity of the W4A4 GEMM on the FP6 matrix cores (K from 8192 to 65536).
+
+The codes enter the block-scaled FP6 MFMA as u = q + 8, the float32
+accumulator holds sum u_a u_b exactly while 225 K < 2^24, and the epilogue
+subtracts the code sums; the int32 accumulators must equal the oracle's
+int64 product bit for bit, the outputs the oracle epilogue on them.  The
+cases cover ragged M and N (rows and columns past the last full tile), the
+largest K the path takes with every code at +-7 and with -8 nibbles (u = 0,
+accepted by the ABI), and the first K past the limit (the int8 kernels).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.test_gpu_parity import check_gemm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rotation_bit_quantization_amd import spin
+    spin.load()
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 5, 8192), (37, 53, 8192), (257, 300, 8192), (300, 200, 12288),
+                                   (600, 1000, 16384), (4096 + 37, 256 + 3, 12288), (1000, 1030, 8320)])
+def test_gemm_fp6_ragged(M, N, K):
+    rng = np.random.default_rng(M * 31 + N + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw)
+
+
+@pytest.mark.parametrize("K", [65536, 65536 + 128])
+def test_gemm_fp6_largest_k_extremes(K):
+    """K = 65536 is the largest the FP6 path takes (225 K < 2^24); every code +-7
+    gives |acc| = 49 K, -8 nibbles give u = 0 against u = 15; one more k-step
+    runs the int8 kernels."""
+    M, N = 20, 7
+    rng = np.random.default_rng(K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    qx[0] = 7
+    qx[1] = -7
+    qx[2] = -8                                   # u = 0
+    qx[3, ::2] = -8
+    qx[3, 1::2] = 7
+    qw[0] = 7                                    # u = 15
+    qw[1] = -7
+    qw[2] = -8
+    _, a = check_gemm(qx, qw, np.ones(M, np.float32), np.ones(N, np.float32))
+    assert a[0, 0] == 49 * K and a[1, 0] == -49 * K and a[0, 1] == -49 * K
+    assert a[2, 2] == 64 * K and a[2, 0] == -56 * K
