@@ -24,21 +24,37 @@
 // unchanged.
 //
 // w4a4_gemm_fp6: 256 x 256 output tile per workgroup of 8 waves (two per
-// SIMD), each wave 128 x 64 as 4 x 2 tiles of the 32x32x64 MFMA.  A K step is
-// 128 codes (two MFMA k-steps).  Every thread owns four 16-byte chunks per
-// step (chunk c = lane / 16 of rows 16 w + lane % 16 and +128, of A and of
-// B); it loads them two steps ahead into registers, converts them once for
-// the whole workgroup, adds their code sums to four per-row counters and
-// writes the FP6 fields to a double-buffered LDS stage.  Each wave then reads
-// its operands from the stage (lane l: row l % 32, k-half l / 32).
-// LDS layout of a stage: regions of 32 rows x 32 bytes indexed by (k-step,
-// block of 32 rows, k-half); a row holds its six dwords of fields and two
-// unused ones as two 16-byte halves, swapped in rows 8-15 of every 16 so that
-// the 16-lane groups of a 16-byte read touch 16 distinct bank groups.  A lane
-// reads its operand with two 16-byte LDS reads straight into the registers
-// the MFMA takes.  One barrier per step.  Rows beyond M or N load the last
-// row; their results are never stored.  Tiles are ordered XCD-aware as in the
-// int8 kernels.
+// SIMD), each wave 128 x 64 as 4 x 2 tiles of the 32x32x64 MFMA; a step is 128
+// codes (two MFMA k-steps) and ends in the one barrier of the step.
+//   * Thread (w, l) owns k-half l / 32 of both k-steps of row 32 w + l % 32
+//     of A and of B: four 16-byte chunks per step, loaded from global memory
+//     into registers one step ahead (lanes l and l + 32 read one 32-byte row
+//     segment, the two k-steps of a row are adjacent).  Each code is
+//     converted once for the whole workgroup.
+//   * The fields go to a double-buffered LDS stage as regions of 32 rows x
+//     24 bytes indexed by (k-step, block of 32 rows, k-half); lane l of a
+//     wave reads row l % 32 of the k-half l / 32 region (24-byte rows: the
+//     8-byte accesses of 16 or 32 consecutive rows hit distinct banks).
+//   * Every operand of a k-step is read from its own base register so that
+//     the compiler does not pair 8-byte reads of different operands (the
+//     pair would then have to be moved into the MFMA's register tuple).
+//   * The conversion of the next step is interleaved by hand with the 16
+//     MFMAs of the current one (half a chunk after every second MFMA, fenced
+//     by scheduling barriers, the results pinned in place) so that the
+//     matrix cores and the vector ALU work at the same time; the LDS writes
+//     follow the step's last operand read.
+// Rows beyond M or N load the last row; their results are never stored.
+// Tiles are ordered XCD-aware as in the int8 kernels.
+//
+// Measured on MI355X (random codes, 4096 x 4096 x 12288): the LDS traffic of
+// a step (147 KB of operand reads and 48 KB of field writes per CU) exceeds
+// the 1024 cycles of MFMA work per SIMD at 128 bytes per clock, so the kernel
+// is LDS-bound at about a third of the FP6 rate; it still beats the int8
+// kernels on long reductions (K >= 8192).  Designs measured slower: one wave
+// per SIMD with 128 x 128 wave tiles (258 against 182 us: a single wave
+// overlaps neither its ALU work with its MFMAs nor LDS latency), 64-code
+// steps (one barrier per 8 MFMAs per wave), raw codes staged in LDS by DMA
+// (extra LDS traffic), and 32-byte LDS rows (one third more operand bytes).
 #include "gemm_common.h"
 #include "spin_device.h"
 #include "spin_internal.h"
