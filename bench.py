@@ -12,7 +12,9 @@ step reads activations that the 256 MB Infinity Cache no longer holds.
 Prints ONE JSON line.  `value` is fwht_quant's achieved GB/s (algorithmic
 bytes per launch / mean launch time, from HIP events on the launch stream);
 the GEMM's TOPS follow in `gemm_tops`; `roofline` describes the kernel that
-dominates the step (the GEMM) and `roofline_fwht_quant` the other one.
+dominates the step (the GEMM, against the dense INT8 peak the metric names and,
+in `issued`, against the dense FP6 peak of the instruction it issues) and
+`roofline_fwht_quant` the other one.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--gpus 1]
@@ -32,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
+FP6_PEAK_TOPS = 10100.0       # MI355X dense FP6 / FP4 MFMA (the instruction the down_proj GEMM issues)
 M, K, N, HAD_N = 4096, 12288, 4096, 12288
 FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
 # The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2180.2
@@ -56,11 +59,12 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
     "fwht_quant": {"sources": {"fwht_quant.hip": "0be8bc922ec664bc", "spin_device.h": "bbe2e2331921046d"},
-                  "read": 101805533, "write": 25297045},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "d00bf9c0b6026fbd", "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "bbe2e2331921046d"},
-                 "read": 151262079, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "68f3dc301d7673ca", "spin_device.h": "bbe2e2331921046d"},
-                "read": 33636265, "write": 8650752},
+                  "read": 101818183, "write": 25297008},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "a180deb96cefad8b", "w4a4_gemm_fp6.hip": "dcff8962850f1d08",
+                              "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "bbe2e2331921046d"},
+                 "read": 151586563, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "323482a3630af890", "spin_device.h": "bbe2e2331921046d"},
+                "read": 33636638, "write": 8650752},
 }
 
 
@@ -168,12 +172,15 @@ def machine_ceilings(fwht_tbps, gemm_tops):
     from rotation_bit_quantization_amd import machine
     i8 = machine.mfma_rate(0)
     f16 = machine.mfma_rate(1)
+    f6 = machine.mfma_rate(2)
     rd = machine.read_bandwidth()
     return {
         "mfma_i32_32x32x32_i8": {"tops": round(i8["tops"], 1), "clock_ghz": round(i8["clock_ghz"], 3)},
         "mfma_f32_32x32x16_f16": {"tflops": round(f16["tops"], 1), "clock_ghz": round(f16["clock_ghz"], 3)},
+        "mfma_scale_f32_32x32x64_fp6": {"tops": round(f6["tops"], 1), "clock_ghz": round(f6["clock_ghz"], 3)},
         "hbm_read_tbps": round(rd["tbps"], 3),
         "w4a4_gemm_frac_of_measured_int8": round(gemm_tops / i8["tops"], 4),
+        "w4a4_gemm_frac_of_measured_fp6": round(gemm_tops / f6["tops"], 4),
         "fwht_quant_frac_of_measured_read": round(fwht_tbps / rd["tbps"], 4),
         "note": "measured on this GPU; the roofline objects keep the published peaks",
     }
@@ -192,14 +199,21 @@ def extra_workloads(args, dev, stream):
     from rotation_bit_quantization_amd import checks
     r1 = torch.from_numpy(q["r"]).to(dev)
     out["rotation_inputs_orthogonality"] = {"R1 Haar 4096 (qkv_proj)": checks.orthogonality_error(r1)}
-    _, Wq, ws = spin.spin_fold_rotation(torch.from_numpy(q["w"]).to(dev), r1, 4096)
-    X = torch.from_numpy(q["x"]).to(dev)
-    Xq, xs, _ = spin.spin_fwht_quant(X, 1)
-    Y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        spin.spin_w4a4_gemm(Xq, xs, Wq, ws, Y=Y)
-    t_q = _time(lambda i: spin.spin_fwht_quant(X, 1, Xq=Xq, x_scale=xs), reps, stream)
-    t_g = _time(lambda i: spin.spin_w4a4_gemm(Xq, xs, Wq, ws, Y=Y), reps, stream)
+    _, Wq0, ws = spin.spin_fold_rotation(torch.from_numpy(q["w"]).to(dev), r1, 4096)
+    # buffer sets rotate as for the headline step, so that operands come from HBM
+    sets = max(1, args.sets)
+    X = [torch.from_numpy(q["x"]).to(dev)] + [None] * (sets - 1)
+    for i in range(1, sets):
+        X[i] = X[0].clone()
+    Wq = [Wq0] + [Wq0.clone() for _ in range(1, sets)]
+    qs = [spin.spin_fwht_quant(x, 1) for x in X]
+    Xq, xs = [t[0] for t in qs], [t[1] for t in qs]
+    Y = [torch.empty((4096, 6144), dtype=torch.float32, device=dev) for _ in range(sets)]
+    for i in range(args.warmup):
+        spin.spin_w4a4_gemm(Xq[i % sets], xs[i % sets], Wq[i % sets], ws, Y=Y[i % sets])
+    t_q = _time(lambda i: spin.spin_fwht_quant(X[i % sets], 1, Xq=Xq[i % sets], x_scale=xs[i % sets]), reps, stream)
+    t_g = _time(lambda i: spin.spin_w4a4_gemm(Xq[i % sets], xs[i % sets], Wq[i % sets], ws, Y=Y[i % sets]), reps,
+                stream)
     out["qkv_proj"] = {"workload": "X 4096x4096 fp16 quant-only, W 4096x6144 (R1 4096 folded), M=4096",
                        "quant_us": t_q * 1e3, "gemm_us": t_g * 1e3,
                        "gemm_tops": 2.0 * 4096 * 6144 * 4096 / (t_g * 1e-3) / 1e12,
@@ -294,10 +308,15 @@ def w4a8_workloads(args, dev, stream):
            "gemm_frac_of_int8_peak": 2.0 * M * N * K / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS}
     del X, q, Y
     kv = synth.kv_config()
-    Kd = torch.from_numpy(kv["k"]).to(dev)
-    codes = torch.empty((KV_T, KV_H, KV_D), dtype=torch.int8, device=dev)
-    sc = torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev)
-    t_k = _time(lambda i: spin.spin_kv_quant8(Kd, 1, codes=codes, scale=sc), reps, stream)
+    Kd = [torch.from_numpy(kv["k"]).to(dev)] + [None] * (sets - 1)
+    for i in range(1, sets):
+        Kd[i] = Kd[0].clone()
+    codes = [torch.empty((KV_T, KV_H, KV_D), dtype=torch.int8, device=dev) for _ in range(sets)]
+    sc = [torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev) for _ in range(sets)]
+    for i in range(args.warmup):
+        spin.spin_kv_quant8(Kd[i % sets], 1, codes=codes[i % sets], scale=sc[i % sets])
+    t_k = _time(lambda i: spin.spin_kv_quant8(Kd[i % sets], 1, codes=codes[i % sets], scale=sc[i % sets]), reps,
+                stream)
     kbytes = KV_T * KV_H * (2 * KV_D + KV_D + 2)
     out["kv_quant8_us"] = t_k * 1e3
     out["kv_quant8_GBps"] = kbytes / (t_k * 1e-3) / 1e9
@@ -465,7 +484,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32+i8",
+        # what the path computes in: the Hadamard's 32-point stages on fp16
+        # matrix cores (fp16 row, fp32 intermediate as an fp16 hi + lo pair,
+        # fp32 accumulation), the rest of the transform and the quantizer in
+        # fp32; the GEMM on INT4 codes carried exactly as FP6 E2M3 operands
+        # (fp32 accumulation of integer products), epilogue in fp32
+        "dtype": "fwht: f16 MFMA (hi+lo) + f32; gemm: int4 codes as FP6-E2M3 MFMA, exact f32 acc",
         "data": "synthetic (seeded N(0,1) activations, 0.1% channels x100; N(0,0.02) weights)",
         "config": {"workload": "R4 down_proj path: fwht_quant X 4096x12288 fp16, had_n 12288 "
                                "(H12 x H1024), per-token INT4; w4a4_gemm M=4096 N=4096 K=12288",
@@ -477,7 +501,9 @@ def main():
         "gemm_frac_of_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
         "roofline": {"kernel": "w4a4_gemm", "bound": "mfma", "achieved": round(gemm_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic("w4a4_gemm")},
+                     "traffic": traffic("w4a4_gemm"),
+                     "issued": {"instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 (FP6 E2M3)",
+                                "peak": FP6_PEAK_TOPS, "frac": round(gemm_tops / FP6_PEAK_TOPS, 4)}},
         "roofline_fwht_quant": {"kernel": "fwht_quant", "bound": "hbm", "achieved": round(fwht_gbps, 2),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(fwht_gbps / HBM_PEAK_GBPS, 4),

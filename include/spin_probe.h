@@ -23,15 +23,18 @@ extern "C" {
 #endif
 
 /* Dense MFMA loop.  kind 0: v_mfma_i32_32x32x32_i8 (65536 ops each, the INT4
- * GEMM's instruction); kind 1: v_mfma_f32_32x32x16_f16 (32768 flops each, the
- * Hadamard stages).  `blocks` workgroups of 256 threads (4 waves); every wave
- * runs `iters` rounds of four independent MFMAs, i.e. 4 * iters instructions.
- * `operands`: 64 lanes x 8 dwords (A in dwords 0-3 of a lane, B in 4-7), the
- * data the matrix cores multiply.  `timing`: 4 int64 per wave (blocks * 4
+ * GEMM's instruction for K < 8192); kind 1: v_mfma_f32_32x32x16_f16 (32768
+ * flops each, the Hadamard stages); kind 2: v_mfma_scale_f32_32x32x64_f8f6f4
+ * with FP6 E2M3 operands and block scales 2^3 (131072 ops each, the INT4 GEMM's
+ * instruction for long reductions).  `blocks` workgroups of 256 threads (4
+ * waves); every wave runs `iters` rounds of four independent MFMAs, i.e.
+ * 4 * iters instructions.  `operands`: the data the matrix cores multiply,
+ * kinds 0 and 1: 64 lanes x 8 dwords (A in dwords 0-3 of a lane, B in 4-7);
+ * kind 2: 64 lanes x 16 dwords (A in dwords 0-5, B in 8-13).  `timing`: 4 int64 per wave (blocks * 4
  * waves): shader-cycle counter at start and end, 100 MHz real-time counter at
  * start and end (the last word may be off by one: it also carries the
  * accumulators so that no chain is optimised away).
- * Errors: SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE (kind not 0/1, blocks or iters
+ * Errors: SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE (kind not 0, 1 or 2, blocks or iters
  * out of [1, 2^20] / [1, 2^24]), SPIN_ERR_MISALIGNED, SPIN_ERR_HIP. */
 spin_status spin_probe_mfma(int kind, int blocks, int iters, const uint32_t* operands, int64_t* timing,
                             void* stream);

@@ -1,7 +1,7 @@
 // Machine probes for the benchmark report (libspin_probe, not part of
 // libspin): the sustained dense MFMA rate of the two instructions the hot path
-// uses, the shader clock while the matrix cores are busy, and the streaming
-// read bandwidth of HBM.  They give the measured ceilings that the kernels'
+// uses (the int8, FP16 and block-scaled FP6 MFMAs), the shader clock while
+// the matrix cores are busy, and the streaming read bandwidth of HBM.  They give the measured ceilings that the kernels'
 // roofline fractions can be read against, beside the published peaks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -15,12 +15,15 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f16f __attribute__((ext_vector_type(16)));
 
 constexpr int kProbeThreads = 256;
 
 // Each wave runs `iters` rounds of four independent MFMA chains on operands
-// taken from `operands` (8 dwords per lane: A in dwords 0-3, B in 4-7), so that
-// the matrix cores see data of the hot path's kind rather than constants.
+// taken from `operands` (kinds 0 and 1: 8 dwords per lane, A in dwords 0-3 and
+// B in 4-7; kind 2: 16 dwords per lane, A in dwords 0-5 and B in 8-13), so
+// that the matrix cores see data of the hot path's kind rather than constants.
 // Lane 0 of every wave records its start and end in shader cycles and in the
 // constant 100 MHz real-time counter.
 template <int KIND>
@@ -28,8 +31,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma(const uint32_t* __re
                                                             int64_t* __restrict__ timing) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6);
-    const u4v a = *reinterpret_cast<const u4v*>(operands + 8 * lane);
-    const u4v b = *reinterpret_cast<const u4v*>(operands + 8 * lane + 4);
+    const int stride = KIND == 2 ? 16 : 8;
+    const u4v a = *reinterpret_cast<const u4v*>(operands + stride * lane);
+    const u4v b = *reinterpret_cast<const u4v*>(operands + stride * lane + (KIND == 2 ? 8 : 4));
     const int64_t c0 = static_cast<int64_t>(__builtin_readcyclecounter());
     const int64_t r0 = static_cast<int64_t>(__builtin_amdgcn_s_memrealtime());
     int check = 0;
@@ -43,6 +47,23 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma(const uint32_t* __re
             acc3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, bv, acc3, 0, 0, 0);
         }
         check = acc0[0] ^ acc1[5] ^ acc2[10] ^ acc3[15];
+    } else if (KIND == 2) {
+        // FP6 E2M3 operands (six dwords each), block scales 2^3, the W4A4
+        // GEMM's instruction for long reductions
+        const u4v a2 = *reinterpret_cast<const u4v*>(operands + stride * lane + 4);
+        const u4v b2 = *reinterpret_cast<const u4v*>(operands + stride * lane + 12);
+        const v8i av = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
+                        static_cast<int>(a2[0]), static_cast<int>(a2[1]), 0, 0};
+        const v8i bv = {static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3]),
+                        static_cast<int>(b2[0]), static_cast<int>(b2[1]), 0, 0};
+        f16f acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+        for (int i = 0; i < iters; ++i) {
+            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc0, 2, 2, 0, 130, 0, 130);
+            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc1, 2, 2, 0, 130, 0, 130);
+            acc2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, av, acc2, 2, 2, 0, 130, 0, 130);
+            acc3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, bv, acc3, 2, 2, 0, 130, 0, 130);
+        }
+        check = __float_as_int(acc0[0] + acc1[5] + acc2[10] + acc3[15]);
     } else {
         const h8v av = __builtin_bit_cast(h8v, a), bv = __builtin_bit_cast(h8v, b);
         f16v acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
@@ -92,13 +113,15 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read(const u4v* __restric
 extern "C" spin_status spin_probe_mfma(int kind, int blocks, int iters, const uint32_t* operands, int64_t* timing,
                                        void* stream) {
     if (!operands || !timing) return SPIN_ERR_NULL;
-    if ((kind != 0 && kind != 1) || blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
+    if (kind < 0 || kind > 2 || blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
         return SPIN_ERR_BAD_SHAPE;
     if ((reinterpret_cast<uintptr_t>(operands) & 15u) || (reinterpret_cast<uintptr_t>(timing) & 15u))
         return SPIN_ERR_MISALIGNED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (kind == 0)
         hipLaunchKernelGGL(probe_mfma<0>, dim3(blocks), dim3(kProbeThreads), 0, s, operands, iters, timing);
+    else if (kind == 2)
+        hipLaunchKernelGGL(probe_mfma<2>, dim3(blocks), dim3(kProbeThreads), 0, s, operands, iters, timing);
     else
         hipLaunchKernelGGL(probe_mfma<1>, dim3(blocks), dim3(kProbeThreads), 0, s, operands, iters, timing);
     return hipGetLastError() == hipSuccess ? SPIN_OK : SPIN_ERR_HIP;

@@ -1,5 +1,5 @@
 """Machine probes through libspin_probe (include/spin_probe.h): the sustained
-dense MFMA rate of the hot path's two matrix instructions with the shader
+dense MFMA rate of the hot path's three matrix instructions with the shader
 clock meanwhile, and the streaming read bandwidth of HBM.  bench.py reports
 them beside the published peaks; nothing in the hot path uses them.
 
@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
 EXPORTED_SYMBOLS = ("spin_probe_mfma", "spin_probe_read")
-OPS_PER_MFMA = {0: 2 * 32 * 32 * 32, 1: 2 * 32 * 32 * 16}     # v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16
+# v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16, v_mfma_scale_f32_32x32x64_f8f6f4 (FP6)
+OPS_PER_MFMA = {0: 2 * 32 * 32 * 32, 1: 2 * 32 * 32 * 16, 2: 2 * 32 * 32 * 64}
 
 
 def library_path() -> str:
@@ -41,12 +42,29 @@ def load():
     return lib
 
 
+def _fp6_fields(u):
+    """32 unsigned 6-bit fields -> six little-endian dwords (field f at bits
+    6f .. 6f + 5 of the 192-bit operand)."""
+    v = 0
+    for f, x in enumerate(u):
+        v |= int(x) << (6 * f)
+    return [(v >> (32 * i)) & 0xFFFFFFFF for i in range(6)]
+
+
 def _operands(kind, seed=5):
-    """64 lanes x 8 dwords of the hot path's kind of data: INT4 codes widened
-    x16 into int8 (kind 0), N(0,1) fp16 (kind 1)."""
+    """The hot path's kind of data for one wave: INT4 codes widened x16 into
+    int8 (kind 0, 64 lanes x 8 dwords), N(0,1) fp16 (kind 1, 64 x 8), INT4
+    codes as FP6 E2M3 fields u = q + 8 (kind 2, 64 x 16: A in dwords 0-5, B in
+    8-13)."""
     rng = np.random.default_rng(seed)
     if kind == 0:
         return (rng.integers(-7, 8, size=64 * 32) * 16).astype(np.int8).view(np.uint32)
+    if kind == 2:
+        out = np.zeros((64, 16), np.uint32)
+        for lane in range(64):
+            out[lane, 0:6] = _fp6_fields(rng.integers(-7, 8, size=32) + 8)
+            out[lane, 8:14] = _fp6_fields(rng.integers(-7, 8, size=32) + 8)
+        return out.reshape(-1)
     return rng.standard_normal(64 * 16).astype(np.float16).view(np.uint32)
 
 

@@ -193,7 +193,8 @@ def test_probe_symbols_and_validation(probe):
         assert hasattr(probe, name)
     NULL, BAD, MIS = 1, 2, 3
     assert probe.spin_probe_mfma(0, 1, 1, None, A, None) == NULL
-    assert probe.spin_probe_mfma(2, 1, 1, A, A, None) == BAD
+    assert probe.spin_probe_mfma(3, 1, 1, A, A, None) == BAD
+    assert probe.spin_probe_mfma(-1, 1, 1, A, A, None) == BAD
     assert probe.spin_probe_mfma(0, 0, 1, A, A, None) == BAD
     assert probe.spin_probe_mfma(1, 1, 0, A, A, None) == BAD
     assert probe.spin_probe_mfma(0, 1, 1, U, A, None) == MIS

@@ -17,7 +17,7 @@ def _gpu():
     machine.load()
 
 
-@pytest.mark.parametrize("kind,peak", [(0, 5033.0), (1, 2517.0)])
+@pytest.mark.parametrize("kind,peak", [(0, 5033.0), (1, 2517.0), (2, 10066.0)])
 def test_mfma_rate_is_below_the_peak_and_the_clock_is_plausible(kind, peak):
     r = machine.mfma_rate(kind, waves_per_cu=8, iters=2000)
     # the published dense peaks at 2.4 GHz bound the rate; a busy chip stays above half of them
