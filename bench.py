@@ -163,6 +163,50 @@ def _time(fn, reps, stream):
     return t
 
 
+def kv_qkv_workload(args, dev, stream, kv, sets):
+    """The KV step of one attention layer in one launch (spin_kv_qkv): K rotated +
+    INT4, V INT4, then the same with Q rotated (fp32 out); against K and V as two
+    spin_kv_quant launches.  Buffer sets rotate as in the timed step."""
+    import torch
+    from rotation_bit_quantization_amd import spin
+    src = {n: torch.from_numpy(kv[n]).to(dev) for n in ("q", "k", "v")}
+    ins = [src] + [{n: t.clone() for n, t in src.items()} for _ in range(sets - 1)]
+    outs = []
+    for _ in range(sets):
+        outs.append({
+            "K_codes": torch.empty((KV_T, KV_H, KV_D // 2), dtype=torch.uint8, device=dev),
+            "K_scale": torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev),
+            "V_codes": torch.empty((KV_T, KV_H, KV_D // 2), dtype=torch.uint8, device=dev),
+            "V_scale": torch.empty((KV_T, KV_H), dtype=torch.float16, device=dev),
+            "Q_rot": torch.empty((KV_T, KV_H, KV_D), dtype=torch.float32, device=dev)})
+
+    def kv_one(i):
+        j = i % sets
+        spin.spin_kv_qkv(ins[j]["k"], ins[j]["v"], out=outs[j])
+
+    def qkv_one(i):
+        j = i % sets
+        spin.spin_kv_qkv(ins[j]["k"], ins[j]["v"], ins[j]["q"], out=outs[j])
+
+    def kv_two(i):
+        j = i % sets
+        o = outs[j]
+        spin.spin_kv_quant(ins[j]["k"], 1, codes=o["K_codes"], scale=o["K_scale"])
+        spin.spin_kv_quant(ins[j]["v"], 0, codes=o["V_codes"], scale=o["V_scale"])
+
+    res = {"workload": "K, V [4096][32][128] fp16 (R3 H_128 on K, INT4 + fp16 scale both); Q [4096][32][128] "
+                       "rotated to fp32"}
+    kv_bytes = 2 * KV_T * KV_H * KV_BYTES_PER_GROUP
+    q_bytes = KV_T * KV_H * (2 * KV_D + 4 * KV_D)
+    for name, fn, nbytes in (("kv_one_launch", kv_one, kv_bytes), ("kv_two_launches", kv_two, kv_bytes),
+                             ("qkv_one_launch", qkv_one, kv_bytes + q_bytes)):
+        for i in range(args.warmup):
+            fn(i)
+        s = _time(fn, args.steps, stream) / 1e3
+        res[name] = {"us": s * 1e6, "GBps": nbytes / s / 1e9, "frac_of_hbm": nbytes / s / 1e9 / HBM_PEAK_GBPS}
+    return res
+
+
 def machine_ceilings(fwht_tbps, gemm_tops):
     """Measured ceilings of this GPU (libspin_probe), reported beside the
     published peaks that the roofline fractions use: the INT8 and FP16 MFMA
@@ -449,6 +493,7 @@ def main():
                              "us": k_s * 1e6, "GBps": kv_bytes / k_s / 1e9,
                              "frac_of_hbm": kv_bytes / k_s / 1e9 / HBM_PEAK_GBPS,
                              "traffic": traffic("kv_quant")}
+        extra["kv_qkv"] = kv_qkv_workload(args, dev, stream, kv, sets)
         del Kd, kc, ksc
 
     machine = None

@@ -126,6 +126,29 @@ spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_
                            const float* w_scale, int M, int N, int K, float* Y,
                            int32_t* acc_out, void* stream);
 
+/* Kernel families for spin_w4a4_gemm_ex. */
+#define SPIN_GEMM_AUTO 0   /* the choice spin_w4a4_gemm makes */
+#define SPIN_GEMM_INT8 1   /* codes widened to int8, int8 matrix cores, int32 accumulation */
+#define SPIN_GEMM_FP6 2    /* codes as FP6 E2M3 (u = q + 8, exact), FP6 matrix cores */
+/* K range of the FP6 kernel: its float32 accumulator of products u_a * u_b <= 225
+   is exact while 225 K < 2^24 (K < 74566; the bound stops at the power of two
+   below), and its pipeline needs two steps of 128 codes. */
+#define SPIN_GEMM_FP6_MIN_K 256
+#define SPIN_GEMM_FP6_MAX_K 65536
+
+/*
+ * spin_w4a4_gemm_ex — spin_w4a4_gemm with the kernel family named: the same
+ * arguments, outputs and guarantees (every family gives the same bits), for
+ * callers that tune the choice for their shapes.  `kernel` is SPIN_GEMM_AUTO,
+ * SPIN_GEMM_INT8 or SPIN_GEMM_FP6.
+ * Errors: SPIN_ERR_UNSUPPORTED for another `kernel` value; with
+ * SPIN_GEMM_FP6, SPIN_ERR_BAD_SHAPE unless K % 128 == 0 and
+ * SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K; otherwise as spin_w4a4_gemm.
+ */
+spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                              const float* w_scale, int M, int N, int K, float* Y,
+                              int32_t* acc_out, int kernel, void* stream);
+
 /*
  * spin_kv_quant — head-wise Hadamard (R3) + INT4 KV cache (page "SpinQuant,
  * Reproduced", Q5: R3 in the KV path is an online Hadamard; abstract: 4-bit
@@ -194,6 +217,36 @@ spin_status spin_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_
  */
 spin_status spin_kv_quant8(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
                            int8_t* codes, uint16_t* scale, float* X_rot, void* stream);
+
+/*
+ * spin_kv_qkv — the KV-path step of one attention layer in a single launch
+ * (page "SpinQuant, Reproduced", Q5: R3 rotates queries and keys online, so
+ * Q . K^T is unchanged, while values carry the folded R2 and are only
+ * quantized; abstract: 4-bit KV cache).
+ *
+ *   Q        [T][Hq][D] float32 / float16, or NULL (no query rotation)
+ *   Q_rot    [T][Hq][D] float32, NULL exactly when Q is NULL   OUTPUT:
+ *            y = q . H_128 / sqrt(128) per (t, h) vector, not quantized
+ *   K, V     [T][Hkv][D], the same dtype as Q; Hq need not equal Hkv
+ *            (grouped-query attention)
+ *   bits     4: packed INT4 codes, [T][Hkv][D/2] bytes, rules of spin_kv_quant;
+ *            8: INT8 codes, [T][Hkv][D] bytes, rules of spin_kv_quant8
+ *   K_codes, K_scale   OUTPUT: codes and fp16 scales of K . H_128 / sqrt(128):
+ *            the same bytes spin_kv_quant(K, rotate = 1) (spin_kv_quant8 at
+ *            bits = 8) writes
+ *   K_rot    [T][Hkv][D] float32 or NULL   OUTPUT: the rotated K values
+ *   V_codes, V_scale   OUTPUT: codes and fp16 scales of V, not rotated: the
+ *            same bytes spin_kv_quant(V, rotate = 0) writes
+ * Requirements: T, Hkv >= 0, Hq >= 0 when Q is non-NULL (ignored otherwise),
+ * D == 128, bits in {4, 8}; K, V and the four K / V outputs non-NULL.
+ * Errors: SPIN_ERR_NULL for a missing pointer or a Q / Q_rot pair with one
+ * NULL, SPIN_ERR_UNSUPPORTED for a dtype or bits value outside the above,
+ * SPIN_ERR_BAD_SHAPE for a size out of range (T * Hkv or T * Hq above 2^34),
+ * SPIN_ERR_MISALIGNED as for every call.
+ */
+spin_status spin_kv_qkv(const void* Q, const void* K, const void* V, spin_dtype x_dtype, int T, int Hq,
+                        int Hkv, int D, int bits, float* Q_rot, uint8_t* K_codes, uint16_t* K_scale,
+                        float* K_rot, uint8_t* V_codes, uint16_t* V_scale, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* spin_status_string(spin_status s);

@@ -115,19 +115,29 @@ spin_status spin_fwht_quant8(const void* X, spin_dtype x_dtype, int M, int K, in
                            stream);
 }
 
-spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
-                           const float* w_scale, int M, int N, int K, float* Y,
-                           int32_t* acc_out, void* stream) {
+spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                              const float* w_scale, int M, int N, int K, float* Y,
+                              int32_t* acc_out, int kernel, void* stream) {
     if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SPIN_ERR_NULL;
+    if (kernel != SPIN_GEMM_AUTO && kernel != SPIN_GEMM_INT8 && kernel != SPIN_GEMM_FP6)
+        return SPIN_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > SPIN_GEMM_MAX_K) return SPIN_ERR_BAD_SHAPE;
+    if (kernel == SPIN_GEMM_FP6 && (K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_GEMM_FP6_MAX_K))
+        return SPIN_ERR_BAD_SHAPE;
     const long long tiles = (static_cast<long long>(M) + 127) / 128 * ((static_cast<long long>(N) + 127) / 128);
     if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(Wq) || !aligned16(w_scale) ||
         !aligned16(Y) || (acc_out && !aligned16(acc_out)))
         return SPIN_ERR_MISALIGNED;
     if (M == 0 || N == 0) return SPIN_OK;
-    return from_hip(spin::launch_w4a4_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out,
+    return from_hip(spin::launch_w4a4_gemm(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, kernel,
                                            static_cast<hipStream_t>(stream)));
+}
+
+spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                           const float* w_scale, int M, int N, int K, float* Y,
+                           int32_t* acc_out, void* stream) {
+    return spin_w4a4_gemm_ex(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, SPIN_GEMM_AUTO, stream);
 }
 
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
@@ -139,6 +149,24 @@ spin_status spin_kv_quant8(const void* X, spin_dtype x_dtype, int T, int H, int 
                            int8_t* codes, uint16_t* scale, float* X_rot, void* stream) {
     return kv_quant_impl(X, x_dtype, T, H, D, rotate, 8, reinterpret_cast<uint8_t*>(codes), scale, X_rot,
                          stream);
+}
+
+spin_status spin_kv_qkv(const void* Q, const void* K, const void* V, spin_dtype x_dtype, int T, int Hq,
+                        int Hkv, int D, int bits, float* Q_rot, uint8_t* K_codes, uint16_t* K_scale,
+                        float* K_rot, uint8_t* V_codes, uint16_t* V_scale, void* stream) {
+    if (!K || !V || !K_codes || !K_scale || !V_codes || !V_scale) return SPIN_ERR_NULL;
+    if ((Q == nullptr) != (Q_rot == nullptr)) return SPIN_ERR_NULL;
+    if (x_dtype != SPIN_F32 && x_dtype != SPIN_F16) return SPIN_ERR_UNSUPPORTED;
+    if (bits != 4 && bits != 8) return SPIN_ERR_UNSUPPORTED;
+    if (T < 0 || Hkv < 0 || (Q && Hq < 0) || D != 128) return SPIN_ERR_BAD_SHAPE;
+    if (static_cast<long long>(T) * Hkv > (1LL << 34)) return SPIN_ERR_BAD_SHAPE;
+    if (Q && static_cast<long long>(T) * Hq > (1LL << 34)) return SPIN_ERR_BAD_SHAPE;
+    if ((Q && (!aligned16(Q) || !aligned16(Q_rot))) || !aligned16(K) || !aligned16(V) || !aligned16(K_codes) ||
+        !aligned16(K_scale) || (K_rot && !aligned16(K_rot)) || !aligned16(V_codes) || !aligned16(V_scale))
+        return SPIN_ERR_MISALIGNED;
+    if (T == 0 || (Hkv == 0 && (!Q || Hq == 0))) return SPIN_OK;
+    return from_hip(spin::launch_kv_qkv(Q, K, V, x_dtype == SPIN_F16, T, Q ? Hq : 0, Hkv, bits, Q_rot, K_codes,
+                                        K_scale, K_rot, V_codes, V_scale, static_cast<hipStream_t>(stream)));
 }
 
 spin_status spin_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_t* Wq,

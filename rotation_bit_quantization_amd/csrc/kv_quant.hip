@@ -92,13 +92,14 @@ __device__ __forceinline__ uint2 kv_codes8(const float* z, float sign, float nor
 // values 8 l .. 8 l + 7 of the transform times (-1)^popcount(l & 7).  The
 // first in-register level reads both fp16 halves with a mixed-precision FMA
 // (`one` = 1.0 passed at run time keeps it an FMA).
+// `block` is the workgroup's index within the tensor X.
 template <int BITS, typename TIn, bool ROTATE, bool QUANT, bool WRITE_ROT>
-__global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
-    const TIn* __restrict__ X, long long groups, float norm, float one, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scale, float* __restrict__ X_rot) {
+__device__ __forceinline__ void kv_vectors(const TIn* __restrict__ X, long long groups, float norm, float one,
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scale,
+                                           float* __restrict__ X_rot, long long block) {
     constexpr int kPer = 2;
     const int l = threadIdx.x & 15;
-    const long long g0 = (static_cast<long long>(blockIdx.x) * kKvGroupsPerBlock + (threadIdx.x >> 4)) * kPer;
+    const long long g0 = (block * kKvGroupsPerBlock + (threadIdx.x >> 4)) * kPer;
     if (g0 >= groups) return;  // the 16 lanes of a group leave together
     const int src = ROTATE ? g_perm(l) : l;
 
@@ -191,6 +192,46 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
     }
 }
 
+template <int BITS, typename TIn, bool ROTATE, bool QUANT, bool WRITE_ROT>
+__global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(
+    const TIn* __restrict__ X, long long groups, float norm, float one, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scale, float* __restrict__ X_rot) {
+    kv_vectors<BITS, TIn, ROTATE, QUANT, WRITE_ROT>(X, groups, norm, one, codes, scale, X_rot, blockIdx.x);
+}
+
+// The KV step of one attention layer: the grid's first bk workgroups take K
+// (rotated and quantized), the next bv take V (quantized only), the rest Q
+// (rotated only).  Each workgroup runs exactly the code of the matching
+// single-tensor kernel, so the outputs are the same bits.
+struct KvQkvArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    long long gq, gk, gv;          // (token, head) vectors per tensor
+    long long bk, bv;              // workgroups of K and of V
+    float norm, one;
+    float* Q_rot;
+    uint8_t* K_codes;
+    uint16_t* K_scale;
+    float* K_rot;
+    uint8_t* V_codes;
+    uint16_t* V_scale;
+};
+
+template <int BITS, typename TIn, bool K_ROT>
+__global__ __launch_bounds__(kKvThreads) void kv_qkv_kernel(KvQkvArgs a) {
+    const long long b = blockIdx.x;
+    if (b < a.bk)
+        kv_vectors<BITS, TIn, true, true, K_ROT>(static_cast<const TIn*>(a.K), a.gk, a.norm, a.one, a.K_codes,
+                                                 a.K_scale, a.K_rot, b);
+    else if (b < a.bk + a.bv)
+        kv_vectors<BITS, TIn, false, true, false>(static_cast<const TIn*>(a.V), a.gv, a.norm, a.one, a.V_codes,
+                                                  a.V_scale, nullptr, b - a.bk);
+    else
+        kv_vectors<BITS, TIn, true, false, true>(static_cast<const TIn*>(a.Q), a.gq, a.norm, a.one, nullptr,
+                                                 nullptr, a.Q_rot, b - a.bk - a.bv);
+}
+
 template <int BITS, typename TIn, bool ROTATE, bool QUANT, bool WR>
 hipError_t launch_kv_t(const TIn* X, long long groups, uint8_t* codes, uint16_t* scale,
                        float* Xr, hipStream_t s) {
@@ -227,7 +268,44 @@ hipError_t launch_kv_bits(const void* X, bool x_f16, long long groups, bool rota
                                            X_rot, s);
 }
 
+template <int BITS, typename TIn>
+hipError_t launch_kv_qkv_t(const KvQkvArgs& a, long long blocks, hipStream_t s) {
+    if (a.K_rot)
+        hipLaunchKernelGGL((kv_qkv_kernel<BITS, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(kKvThreads),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((kv_qkv_kernel<BITS, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(kKvThreads),
+                           0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_kv_qkv(const void* Q, const void* K, const void* V, bool x_f16, int T, int Hq, int Hkv,
+                         int bits, float* Q_rot, uint8_t* K_codes, uint16_t* K_scale, float* K_rot,
+                         uint8_t* V_codes, uint16_t* V_scale, hipStream_t s) {
+    const long long per_block = 2LL * kKvGroupsPerBlock;
+    KvQkvArgs a;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.gq = Q ? static_cast<long long>(T) * Hq : 0;
+    a.gk = a.gv = static_cast<long long>(T) * Hkv;
+    a.bk = a.bv = (a.gk + per_block - 1) / per_block;
+    a.norm = static_cast<float>(1.0 / __builtin_sqrt(128.0));
+    a.one = 1.0f;
+    a.Q_rot = Q_rot;
+    a.K_codes = K_codes;
+    a.K_scale = K_scale;
+    a.K_rot = K_rot;
+    a.V_codes = V_codes;
+    a.V_scale = V_scale;
+    const long long blocks = a.bk + a.bv + (a.gq + per_block - 1) / per_block;
+    if (blocks == 0) return hipSuccess;
+    if (bits == 8)
+        return x_f16 ? launch_kv_qkv_t<8, __half>(a, blocks, s) : launch_kv_qkv_t<8, float>(a, blocks, s);
+    return x_f16 ? launch_kv_qkv_t<4, __half>(a, blocks, s) : launch_kv_qkv_t<4, float>(a, blocks, s);
+}
 
 hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, int bits, uint8_t* codes,
                            uint16_t* scale, float* X_rot, hipStream_t s) {

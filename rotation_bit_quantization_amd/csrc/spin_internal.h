@@ -18,12 +18,19 @@ struct HadOrder {
 hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h, int bits,
                              uint8_t* Xq, float* x_scale, float* X_rot, hipStream_t s);
 
+// kernel: 0 the automatic choice, 1 the int8 kernels, 2 the FP6 kernel
+// (abi.cpp has checked that the FP6 kernel takes K).
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
-                            int32_t* acc_out, hipStream_t s);
+                            int32_t* acc_out, int kernel, hipStream_t s);
 
 hipError_t launch_kv_quant(const void* X, bool x_f16, int T, int H, bool rotate, int bits,
                            uint8_t* codes, uint16_t* scale, float* X_rot, hipStream_t s);
+
+// Q (optional, rotate only), K (rotate + quantize) and V (quantize) in one launch.
+hipError_t launch_kv_qkv(const void* Q, const void* K, const void* V, bool x_f16, int T, int Hq, int Hkv,
+                         int bits, float* Q_rot, uint8_t* K_codes, uint16_t* K_scale, float* K_rot,
+                         uint8_t* V_codes, uint16_t* V_scale, hipStream_t s);
 
 // The FP6 matrix-core path of launch_w4a4_gemm (exact for K <= kGemmFp6MaxK).
 constexpr int kGemmFp6MaxK = 65536;

@@ -478,7 +478,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
 
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
-                            int32_t* acc_out, hipStream_t s) {
+                            int32_t* acc_out, int kernel, hipStream_t s) {
+    if (kernel == 2 || (kernel == 0 && w4a4_gemm_fp6_applies(M, N, K)))
+        return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
     if (M <= 16 && K % 128 == 0) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         // many column groups (gate/up): two waves each, so that every wave
@@ -502,8 +504,6 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
         }
         return hipGetLastError();
     }
-    if (w4a4_gemm_fp6_applies(M, N, K))
-        return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
     if (K % kStepCodes == 0) {
         const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);
         {

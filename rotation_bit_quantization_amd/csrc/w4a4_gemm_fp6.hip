@@ -28,36 +28,46 @@
 // codes (two MFMA k-steps) and ends in the one barrier of the step.
 //   * Thread (w, l) owns k-half l / 32 of both k-steps of row 32 w + l % 32
 //     of A and of B: four 16-byte chunks per step, loaded from global memory
-//     into registers one step ahead (lanes l and l + 32 read one 32-byte row
-//     segment, the two k-steps of a row are adjacent).  Each code is
-//     converted once for the whole workgroup.
-//   * The fields go to a double-buffered LDS stage as regions of 32 rows x
-//     24 bytes indexed by (k-step, block of 32 rows, k-half); lane l of a
-//     wave reads row l % 32 of the k-half l / 32 region (24-byte rows: the
-//     8-byte accesses of 16 or 32 consecutive rows hit distinct banks).
+//     into registers one step before they are converted (lanes l and l + 32
+//     read one 32-byte row segment, the two k-steps of a row are adjacent).
+//     Each code is converted once for the whole workgroup.
+//   * The fields go to a ring of three LDS stages (48 KB each) as regions of
+//     32 rows x 24 bytes indexed by (k-step, block of 32 rows, k-half); lane
+//     l of a wave reads row l % 32 of the k-half l / 32 region (24-byte rows:
+//     the 8-byte accesses of 16 or 32 consecutive rows hit distinct banks).
+//     While step s is multiplied from one stage, step s + 1 is complete in
+//     the next and step s + 2 is converted into the third, so the operands
+//     of the next k-step are read while the current one's MFMAs run: each
+//     A operand is reloaded as soon as its second MFMA has issued, and the
+//     B operands alternate between two register sets.
 //   * Every operand of a k-step is read from its own base register so that
 //     the compiler does not pair 8-byte reads of different operands (the
 //     pair would then have to be moved into the MFMA's register tuple).
-//   * The conversion of the next step is interleaved by hand with the 16
-//     MFMAs of the current one (half a chunk after every second MFMA, fenced
-//     by scheduling barriers, the results pinned in place) so that the
-//     matrix cores and the vector ALU work at the same time; the LDS writes
-//     follow the step's last operand read.
+//   * The conversion of step s + 2 is interleaved by hand with the 16 MFMAs
+//     of step s (half a chunk after every MFMA pair, fenced by scheduling
+//     barriers, the results pinned in place), each chunk's fields written as
+//     soon as they are complete.
 // Rows beyond M or N load the last row; their results are never stored.
 // Tiles are ordered XCD-aware as in the int8 kernels.
 //
-// Measured on MI355X (random codes, 4096 x 4096 x 12288): the LDS traffic of
-// a step (147 KB of operand reads and 48 KB of field writes per CU) exceeds
-// the 1024 cycles of MFMA work per SIMD at 128 bytes per clock, so the kernel
-// is LDS-bound at about a third of the FP6 rate; it still beats the int8
-// kernels on long reductions (K >= 8192).  Designs measured slower: one wave
-// per SIMD with 128 x 128 wave tiles (258 against 182 us: a single wave
-// overlaps neither its ALU work with its MFMAs nor LDS latency), 64-code
-// steps (one barrier per 8 MFMAs per wave), raw codes staged in LDS by DMA
-// (extra LDS traffic), and 32-byte LDS rows (one third more operand bytes).
+// Measured on MI355X (random codes, K = 12288): a step takes about 3500
+// cycles whether 16 or 256 CUs are busy, against 1024 cycles of MFMA work
+// per SIMD.  Timing the kernel with parts of the step removed (in a copy):
+// without the MFMAs it is no faster (the matrix cores are hidden); without
+// the operand reads about 3% faster, with operands that hit in cache 5%,
+// without the barrier 13%; without the conversion and the field writes 43%
+// faster.  The bound is the conversion pipeline (about 120 VALU instructions
+// per wave and step, close to the minimum for this encoding, and the LDS
+// writes that follow them), not the matrix cores.  Designs measured slower:
+// loads three steps ahead (registers spill), one wave per SIMD with
+// 128 x 128 wave tiles (a single wave overlaps neither its ALU work with its
+// MFMAs nor LDS latency), 64-code steps (one barrier per 8 MFMAs per wave),
+// raw codes staged in LDS by DMA (extra LDS traffic), and 32-byte LDS rows
+// (one third more operand bytes).
 #include "gemm_common.h"
 #include "spin_device.h"
 #include "spin_internal.h"
+#include "libspin.h"
 
 namespace spin {
 namespace {
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6(
     const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kF6StageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kF6StageBytes];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -197,96 +207,113 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6(
         chunk_to_fp6(p[3], o, sumB);
         put(st + kF6KsBytes + dstB, o);
     };
-    auto mma = [&](int stage) {
+    // Operands in registers: the four A operands of the k-step being
+    // multiplied (each reloaded with the next k-step's as soon as its second
+    // MFMA has issued) and two sets of the two B operands (k-steps alternate).
+    v8i fa[4], fbx[2], fby[2];
+    auto read_a = [&](uint32_t off) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int off = stage * kF6StageBytes + ks * kF6KsBytes;
-            const v8i fb0 = frag(off, 4), fb1 = frag(off, 5);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v8i fa = frag(off, i);
-                acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb0, acc[i][0], 2, 2, 0, kF6Scale,
-                                                                          0, kF6Scale);
-                acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb1, acc[i][1], 2, 2, 0, kF6Scale,
-                                                                          0, kF6Scale);
-            }
-        }
+        for (int i = 0; i < 4; ++i) fa[i] = frag(off, i);
     };
-    // One step: the loads of the step after next into the register set the
-    // previous step emptied (clamped at the end: the last step is loaded
-    // again), the MFMAs on the current stage and the conversion of the next
-    // step (loaded one step ago) into the other stage, in one basic block,
-    // then one barrier.  The conversion is interleaved with the MFMAs (one
-    // MFMA, then a share of the conversion's ALU work and one LDS write) so
-    // that the matrix cores and the vector ALU work at the same time.
-    // The conversion is interleaved with the MFMAs by hand: each region
-    // between scheduling fences holds two MFMAs and half of one chunk's
-    // conversion, so the matrix cores and the vector ALU work at the same
-    // time; the LDS writes of the fields follow the last operand reads of the
-    // step (the compiler cannot tell the two stages apart).
+    // Half of chunk c's conversion (sum of eight codes, three dwords of fields)
+    auto conv_half = [&](const uint4* p, int c, int half, uint32_t* o) {
+        const uint4 q = p[c];
+        int& sum = c < 2 ? sumA : sumB;
+        const uint32_t a = half ? q.z : q.x, b = half ? q.w : q.y;
+        sum = __builtin_amdgcn_sdot8(static_cast<int>(a), 0x11111111, sum, false);
+        sum = __builtin_amdgcn_sdot8(static_cast<int>(b), 0x11111111, sum, false);
+        spread16(a ^ 0x88888888u, b ^ 0x88888888u, o + 3 * half);
+        pin3(o + 3 * half);
+    };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto body = [&](int s, int stage, uint4* p_next, uint4* p_free) {
-        load(min(s + 2, steps - 1), p_free);
-        uint8_t* st = lds + (stage ^ 1) * kF6StageBytes;
-        uint32_t o[4][6];
-        int* sum[4] = {&sumA, &sumA, &sumB, &sumB};
+    // chunk c of a step: A k-step 0, A k-step 1, B k-step 0, B k-step 1
+    auto chunk_dst = [&](uint32_t stage_off, int c) {
+        return lds + stage_off + (c & 1) * kF6KsBytes + (c < 2 ? dstA : dstB);
+    };
+    // One step s: the MFMAs of its two k-steps from stage `cur` (the first
+    // k-step's operands already in registers), with
+    //   * the second k-step's operands read while the first's MFMAs run, and
+    //     the next step's first k-step read (stage `nxt`, complete since the
+    //     previous barrier) while the second's run;
+    //   * CONV: the conversion of step s + 2 (registers p_conv) into stage
+    //     `dst`, interleaved with the MFMAs, and the loads of step s + 3 into
+    //     p_load;
+    // then one barrier.  Three stages: while step s is multiplied from one,
+    // the next is complete in another and step s + 2 is written to the third.
+    auto body = [&](int s, uint32_t cur, uint32_t nxt, uint32_t dst, const uint4* p_conv, uint4* p_load,
+                    bool conv, bool prefetch) {
+        if (conv) load(min(s + 3, steps - 1), p_load);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int off = stage * kF6StageBytes + ks * kF6KsBytes;
-            const v8i fb0 = frag(off, 4), fb1 = frag(off, 5);
-            v8i fa[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = frag(off, i);
+            v8i* fb = ks == 0 ? fbx : fby;        // this k-step's B operands
+            v8i* fbn = ks == 0 ? fby : fbx;       // the next k-step's
+            const uint32_t noff = ks == 0 ? cur + kF6KsBytes : nxt;   // where the next k-step lies
+            const bool more = ks == 0 || prefetch;
+            if (more) {
+                fbn[0] = frag(noff, 4);
+                fbn[1] = frag(noff, 5);
+            }
             fence();
+            uint32_t o[6];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb0, acc[i][0], 2, 2, 0, kF6Scale,
-                                                                          0, kF6Scale);
-                acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb1, acc[i][1], 2, 2, 0, kF6Scale,
-                                                                          0, kF6Scale);
-                const int c = 2 * ks + (i >> 1);               // chunk converted around these MFMAs
-                const uint4 q = p_next[c];
-                if ((i & 1) == 0) {
-                    *sum[c] = __builtin_amdgcn_sdot8(static_cast<int>(q.x), 0x11111111, *sum[c], false);
-                    *sum[c] = __builtin_amdgcn_sdot8(static_cast<int>(q.y), 0x11111111, *sum[c], false);
-                    spread16(q.x ^ 0x88888888u, q.y ^ 0x88888888u, o[c]);
-                    pin3(o[c]);
-                } else {
-                    *sum[c] = __builtin_amdgcn_sdot8(static_cast<int>(q.z), 0x11111111, *sum[c], false);
-                    *sum[c] = __builtin_amdgcn_sdot8(static_cast<int>(q.w), 0x11111111, *sum[c], false);
-                    spread16(q.z ^ 0x88888888u, q.w ^ 0x88888888u, o[c] + 3);
-                    pin3(o[c] + 3);
+                acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[0], acc[i][0], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[1], acc[i][1], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                if (more) fa[i] = frag(noff, i);
+                if (conv) {
+                    const int c = 2 * ks + (i >> 1);
+                    conv_half(p_conv, c, i & 1, o);
+                    if (i & 1) put(chunk_dst(dst, c), o);
                 }
                 fence();
             }
         }
-        put(st + dstA, o[0]);
-        put(st + kF6KsBytes + dstA, o[1]);
-        put(st + dstB, o[2]);
-        put(st + kF6KsBytes + dstB, o[3]);
         barrier_lds();
     };
 
-    // prologue: step 0 converted into stage 0, step 1 in registers
+    // prologue: steps 0 and 1 converted into stages 0 and 1, step 2 in
+    // registers, the operands of step 0's first k-step read
     uint4 P0[4], P1[4];
     load(0, P0);
     load(min(1, steps - 1), P1);
     convert(0, P0);
+    load(min(2, steps - 1), P0);
+    convert(1, P1);
     barrier_lds();
+    fbx[0] = frag(0, 4);
+    fbx[1] = frag(0, 5);
+    read_a(0);
+    // every body starts with no LDS access in flight (each ends in a
+    // barrier that waits for them); so does the loop's first, and the first
+    // MFMA need not wait for the reads a body issues ahead of it
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 
-    // two steps per iteration so that the stages and register sets are fixed;
-    // the last step only multiplies
+    // steps 0 .. steps - 3 convert step s + 2; two per iteration so that the
+    // register sets are fixed; the stage offsets rotate
+    uint32_t cur = 0, nxt = kF6StageBytes, dst = 2 * kF6StageBytes;
+    auto rotate = [&] {
+        const uint32_t t = cur;
+        cur = nxt;
+        nxt = dst;
+        dst = t;
+    };
     int s = 0;
-    for (; s + 2 < steps; s += 2) {
-        body(s, 0, P1, P0);
-        body(s + 1, 1, P0, P1);
+    for (; s + 3 < steps; s += 2) {
+        body(s, cur, nxt, dst, P0, P1, true, true);
+        rotate();
+        body(s + 1, cur, nxt, dst, P1, P0, true, true);
+        rotate();
     }
-    if (s + 1 < steps) {
-        body(s, 0, P1, P0);
-        mma(1);
-    } else {
-        mma(0);
+    if (s + 2 < steps) {
+        body(s, cur, nxt, dst, P0, P1, true, true);
+        rotate();
+        ++s;
     }
+    body(s, cur, nxt, dst, P0, P1, false, true);
+    rotate();
+    body(s + 1, cur, nxt, dst, P0, P1, false, false);
 
     // code sums per operand row (A rows at 0..255, B at 256..511): the two
     // halves of a row sit in lanes l and l + 32; through the idle first stage
@@ -330,17 +357,33 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6(
 
 }  // namespace
 
-// Measured on MI355X against the int8 kernels (random codes): faster for the
-// long reductions of the down projection (K = 12288: 182 against 207 us at
-// 4096 x 4096), slower for K = 4096 with wide N and for small M.
+// Measured on MI355X against the int8 kernels (random codes, µs):
+//   M x N x K             FP6     int8
+//   4096 x 4096 x 12288   172.9   198.5
+//   8192 x 4096 x 12288   367.8   373.6
+//   4096 x 4096 x 8192    122.9   131.9
+//   16384 x 4096 x 12288  725.0   703.7
+//   2048 x 4096 x 12288   153.9   146.9   (128 tiles: half the CUs)
+//   256 x 4096 x 12288    140.5   128.8
+//   4096 x 6144 x 4096    143.5   122.3   (K = 4096: int8, 256 x 384 tiles)
+// The FP6 kernel wins on long reductions whose 256 x 256 tiles fill one or
+// two rounds of the compute units; with fewer tiles the int8 kernels' shorter
+// per-tile latency wins, with many rounds their higher sustained rate.
 bool w4a4_gemm_fp6_applies(int M, int N, int K) {
-    (void)N;
-    return M > 16 && K % kF6StepCodes == 0 && K >= 8192 && K <= kGemmFp6MaxK;
+    if (M <= 16 || K % kF6StepCodes != 0 || K < 8192 || K > kGemmFp6MaxK) return false;
+    const int cus = device_cu_count();
+    if (cus <= 0) return false;
+    const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
+    return 4 * tiles >= 3LL * cus && tiles <= 2LL * cus;
 }
 
 hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                                 const float* w_scale, int M, int N, int K, float* Y,
                                 int32_t* acc_out, hipStream_t s) {
+    // the pipeline converts two steps before the first multiplication
+    static_assert(SPIN_GEMM_FP6_MIN_K == 2 * kF6StepCodes && SPIN_GEMM_FP6_MAX_K == kGemmFp6MaxK,
+                  "the FP6 K range of the ABI");
+    if (K % kF6StepCodes != 0 || K < 2 * kF6StepCodes || K > kGemmFp6MaxK) return hipErrorInvalidValue;
     const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
     const dim3 grid(static_cast<unsigned>(tiles));
     if (acc_out)

@@ -18,14 +18,16 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
+           "spin_kv_qkv", "spin_w4a4_gemm_ex", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
     SPIN_ERR_HIP = range(6)
 SPIN_F32, SPIN_F16 = 0, 1
+SPIN_GEMM_AUTO, SPIN_GEMM_INT8, SPIN_GEMM_FP6 = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
-                    "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
+                    "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,12 +59,14 @@ def load():
     lib.spin_fold_rotation.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp]
     lib.spin_fwht_quant.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a4_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.spin_w4a4_gemm_ex.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, i, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant8.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
+    lib.spin_kv_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
     for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
-                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8"):
+                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex"):
         getattr(lib, name).restype = ctypes.c_int
     lib.spin_status_string.argtypes = [ctypes.c_int]
     lib.spin_status_string.restype = ctypes.c_char_p
@@ -148,8 +152,12 @@ def spin_fwht_quant(X, had_n, Xq=None, x_scale=None, X_rot=None, want_rot=False,
     return Xq, x_scale, X_rot
 
 
-def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=False, stream=None):
-    """Packed Xq [M, K/2], Wq [N, K/2] + scales -> (Y [M, N] fp32, acc [M, N] int32 or None)."""
+def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=False, kernel=None,
+                   stream=None):
+    """Packed Xq [M, K/2], Wq [N, K/2] + scales -> (Y [M, N] fp32, acc [M, N] int32 or None).
+
+    ``kernel`` (SPIN_GEMM_INT8 / SPIN_GEMM_FP6) names the kernel family through
+    spin_w4a4_gemm_ex; None leaves the choice to the library."""
     _check(Xq, "Xq", (torch.uint8,))
     _check(Wq, "Wq", (torch.uint8,))
     M, Kh = Xq.shape
@@ -165,9 +173,14 @@ def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=Fals
     _check(Y, "Y", (torch.float32,), (M, N))
     if acc_out is not None:
         _check(acc_out, "acc_out", (torch.int32,), (M, N))
-    st = load().spin_w4a4_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, 2 * Kh,
-                               _ptr(Y), _ptr(acc_out), _stream(stream))
-    _raise("spin_w4a4_gemm", st)
+    if kernel is None:
+        st = load().spin_w4a4_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, 2 * Kh,
+                                   _ptr(Y), _ptr(acc_out), _stream(stream))
+        _raise("spin_w4a4_gemm", st)
+    else:
+        st = load().spin_w4a4_gemm_ex(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, 2 * Kh,
+                                      _ptr(Y), _ptr(acc_out), int(kernel), _stream(stream))
+        _raise("spin_w4a4_gemm_ex", st)
     return Y, acc_out
 
 
@@ -259,3 +272,53 @@ def spin_kv_quant8(X, rotate, quantize=True, codes=None, scale=None, X_rot=None,
                                _ptr(scale), _ptr(X_rot), _stream(stream))
     _raise("spin_kv_quant8", st)
     return codes, scale, X_rot
+
+
+def spin_kv_qkv(K, V, Q=None, bits=4, want_k_rot=False, out=None, stream=None):
+    """One launch for a layer's KV step: K [T, Hkv, 128] rotated + quantized, V [T, Hkv, 128]
+    quantized, Q [T, Hq, 128] (optional) rotated.
+
+    Returns a dict with ``K_codes``, ``K_scale``, ``V_codes``, ``V_scale`` (scales as float16
+    tensors holding the fp16 bit patterns), ``Q_rot`` (or None) and ``K_rot`` (or None).
+    Codes are [T, Hkv, 64] uint8 at bits=4 and [T, Hkv, 128] int8 at bits=8.  ``out`` may
+    hold preallocated tensors under the same names; missing ones are allocated.
+    """
+    _check(K, "K", (torch.float16, torch.float32))
+    T, Hkv, D = K.shape
+    _check(V, "V", (K.dtype,), (T, Hkv, D))
+    Hq = 0
+    if Q is not None:
+        _check(Q, "Q", (K.dtype,))
+        if Q.dim() != 3 or Q.shape[0] != T or Q.shape[2] != D:
+            raise ValueError(f"Q has shape {tuple(Q.shape)}, expected ({T}, Hq, {D})")
+        Hq = Q.shape[1]
+    dev = K.device
+    if bits == 4:
+        cshape, cdtype = (T, Hkv, D // 2), torch.uint8
+    elif bits == 8:
+        cshape, cdtype = (T, Hkv, D), torch.int8
+    else:
+        raise ValueError("bits must be 4 or 8")
+    want = {
+        "K_codes": (cshape, cdtype),
+        "K_scale": ((T, Hkv), torch.float16),
+        "V_codes": (cshape, cdtype),
+        "V_scale": ((T, Hkv), torch.float16),
+    }
+    if Q is not None:
+        want["Q_rot"] = ((T, Hq, D), torch.float32)
+    if want_k_rot:
+        want["K_rot"] = ((T, Hkv, D), torch.float32)
+    given = dict(out or {})
+    res = {"Q_rot": None, "K_rot": None}
+    for name, (shape, dtype) in want.items():
+        t = given.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        _check(t, name, (dtype,), shape)
+        res[name] = t
+    st = load().spin_kv_qkv(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(K), T, Hq, Hkv, D, int(bits),
+                            _ptr(res["Q_rot"]), _ptr(res["K_codes"]), _ptr(res["K_scale"]),
+                            _ptr(res["K_rot"]), _ptr(res["V_codes"]), _ptr(res["V_scale"]), _stream(stream))
+    _raise("spin_kv_qkv", st)
+    return res

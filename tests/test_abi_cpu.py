@@ -161,6 +161,63 @@ def test_kv_quant8_validation(lib):
     assert call(H=0) == spin.SPIN_OK
 
 
+def test_gemm_ex_validation(lib):
+    f = lib.spin_w4a4_gemm_ex
+
+    def call(M=4, N=4, K=8192, kernel=spin.SPIN_GEMM_FP6, y=A):
+        return f(A, A, A, A, M, N, K, y, None, kernel, None)
+
+    assert call(kernel=3) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(kernel=-1) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(K=128) == spin.SPIN_ERR_BAD_SHAPE                 # below the FP6 pipeline's two steps
+    assert call(K=8192 + 64) == spin.SPIN_ERR_BAD_SHAPE           # not a multiple of 128
+    assert call(K=65536 + 128) == spin.SPIN_ERR_BAD_SHAPE         # beyond exact float32 accumulation
+    assert call(K=65536 + 128, kernel=spin.SPIN_GEMM_INT8, y=None) == spin.SPIN_ERR_NULL
+    assert call(K=65536 + 128, kernel=spin.SPIN_GEMM_INT8, M=0) == spin.SPIN_OK
+    assert call(K=256, M=0) == spin.SPIN_OK
+    assert call(y=None) == spin.SPIN_ERR_NULL
+    assert call(y=U) == spin.SPIN_ERR_MISALIGNED
+
+
+def test_gemm_fp6_k_range_is_the_float32_limit():
+    """SPIN_GEMM_FP6_MAX_K: the float32 accumulator of products u_a * u_b <= 225
+    (u = q + 8 in [0, 15]) is exact while 225 K stays below 2^24 (K < 74566);
+    the library stops at the power of two below that."""
+    text = open(HEADER).read()
+    kmax = int(re.search(r"#define SPIN_GEMM_FP6_MAX_K (\d+)", text).group(1))
+    kmin = int(re.search(r"#define SPIN_GEMM_FP6_MIN_K (\d+)", text).group(1))
+    assert kmax % 128 == 0 and 225 * kmax < 2 ** 24
+    assert kmin == 256
+
+
+def test_kv_qkv_validation(lib):
+    f = lib.spin_kv_qkv
+
+    def call(Q=A, K=A, V=A, dt=spin.SPIN_F16, T=4, Hq=4, Hkv=2, D=128, bits=4, qr=A, kc=A, ks=A, kr=None,
+             vc=A, vs=A):
+        return f(Q, K, V, dt, T, Hq, Hkv, D, bits, qr, kc, ks, kr, vc, vs, None)
+
+    for name in ("K", "V", "kc", "ks", "vc", "vs"):
+        assert call(**{name: None}) == spin.SPIN_ERR_NULL, name
+    assert call(qr=None) == spin.SPIN_ERR_NULL                  # Q without Q_rot
+    assert call(Q=None) == spin.SPIN_ERR_NULL                   # Q_rot without Q
+    assert call(dt=2) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(bits=6) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(D=64) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(T=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(Hkv=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(Hq=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(T=1 << 30, Hkv=32) == spin.SPIN_ERR_BAD_SHAPE   # 2^35 vectors
+    assert call(T=1 << 30, Hkv=1, Hq=32) == spin.SPIN_ERR_BAD_SHAPE
+    for name in ("Q", "K", "V", "qr", "kc", "ks", "kr", "vc", "vs"):
+        assert call(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    # Hq is ignored without Q; empty problems enqueue nothing
+    assert call(Q=None, qr=None, Hq=-1, T=0) == spin.SPIN_OK
+    assert call(T=0) == spin.SPIN_OK
+    assert call(Q=None, qr=None, Hkv=0) == spin.SPIN_OK
+    assert call(Hq=0, Hkv=0) == spin.SPIN_OK
+
+
 def test_gemm8_bound_is_the_int32_limit():
     """SPIN_GEMM8_MAX_K: the largest multiple of 128 with 127 * 7 * 16 * K < 2^31."""
     k = 150912

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
+import oracle  # noqa: F401  (the oracle behind check_gemm)
+from rotation_bit_quantization_amd import spin
 from tests.test_gpu_parity import check_gemm
 
 pytestmark = pytest.mark.gpu
@@ -23,25 +24,50 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from rotation_bit_quantization_amd import spin
     spin.load()
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 5, 8192), (37, 53, 8192), (257, 300, 8192), (300, 200, 12288),
-                                   (600, 1000, 16384), (4096 + 37, 256 + 3, 12288), (1000, 1030, 8320)])
-def test_gemm_fp6_ragged(M, N, K):
-    rng = np.random.default_rng(M * 31 + N + K)
+def _codes(M, N, K, seed):
+    rng = np.random.default_rng(seed)
     qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
     sx = rng.random(M).astype(np.float32)
     sw = (rng.random(N) * 0.01).astype(np.float32)
-    check_gemm(qx, qw, sx, sw)
+    return qx, qw, sx, sw
 
 
-@pytest.mark.parametrize("K", [65536, 65536 + 128])
-def test_gemm_fp6_largest_k_extremes(K):
-    """K = 65536 is the largest the FP6 path takes (225 K < 2^24); every code +-7
-    gives |acc| = 49 K, -8 nibbles give u = 0 against u = 15; one more k-step
+@pytest.mark.parametrize("M,N,K", [(17, 5, 8192), (37, 53, 8192), (257, 300, 8192), (300, 200, 12288),
+                                   (600, 1000, 16384), (4096 + 37, 256 + 3, 12288), (1000, 1030, 8320),
+                                   (1, 1, 256), (40, 70, 384), (33, 300, 640), (300, 31, 4096)])
+def test_gemm_fp6_ragged(M, N, K):
+    """The FP6 kernel named explicitly: ragged tiles, the shortest pipelines
+    (two and three steps of 128 codes) and odd step counts; its outputs must
+    also equal the int8 kernels' bit for bit."""
+    qx, qw, sx, sw = _codes(M, N, K, M * 31 + N + K)
+    y6, a6 = check_gemm(qx, qw, sx, sw, kernel=spin.SPIN_GEMM_FP6)
+    y8, a8 = check_gemm(qx, qw, sx, sw, kernel=spin.SPIN_GEMM_INT8)
+    assert np.array_equal(a6, a8) and np.array_equal(y6, y8)
+
+
+def test_gemm_auto_matches_both_families():
+    """The automatic choice (the FP6 kernel at this shape) gives the same bits."""
+    qx, qw, sx, sw = _codes(1024, 1024 + 64, 8192, 7)
+    y, a = check_gemm(qx, qw, sx, sw, rows=np.arange(0, 1024, 9))
+    y6, a6 = check_gemm(qx, qw, sx, sw, rows=[0], kernel=spin.SPIN_GEMM_FP6)
+    assert np.array_equal(a, a6) and np.array_equal(y, y6)
+
+
+def test_gemm_fp6_k_outside_its_range():
+    qx, qw, sx, sw = _codes(4, 4, 128, 1)
+    with pytest.raises(spin.SpinError) as e:
+        check_gemm(qx, qw, sx, sw, kernel=spin.SPIN_GEMM_FP6)
+    assert e.value.status == spin.SPIN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("K,kernel", [(65536, "fp6"), (65536, "auto"), (65536 + 128, "auto")])
+def test_gemm_fp6_largest_k_extremes(K, kernel):
+    """K = 65536 is the largest the FP6 kernel takes (225 K < 2^24); every code +-7
+    gives |acc| = 49 K, -8 nibbles give u = 0 against u = 15; one more step
     runs the int8 kernels."""
     M, N = 20, 7
     rng = np.random.default_rng(K)
@@ -55,6 +81,7 @@ def test_gemm_fp6_largest_k_extremes(K):
     qw[0] = 7                                    # u = 15
     qw[1] = -7
     qw[2] = -8
-    _, a = check_gemm(qx, qw, np.ones(M, np.float32), np.ones(N, np.float32))
+    kern = spin.SPIN_GEMM_FP6 if kernel == "fp6" else None
+    _, a = check_gemm(qx, qw, np.ones(M, np.float32), np.ones(N, np.float32), kernel=kern)
     assert a[0, 0] == 49 * K and a[1, 0] == -49 * K and a[0, 1] == -49 * K
     assert a[2, 2] == 64 * K and a[2, 0] == -56 * K

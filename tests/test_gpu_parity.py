@@ -275,10 +275,10 @@ def test_fold_qkv_config_r1_full_size_sampled():
 
 # ---------------------------------------------------------------- gemm
 
-def check_gemm(qx, qw, sx, sw, rows=None):
+def check_gemm(qx, qw, sx, sw, rows=None, kernel=None):
     Xq, Wq = _dev(oracle.pack_int4(qx)), _dev(oracle.pack_int4(qw))
-    Y, acc = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw), want_acc=True)
-    Y2, _ = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw))
+    Y, acc = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw), want_acc=True, kernel=kernel)
+    Y2, _ = spin.spin_w4a4_gemm(Xq, _dev(sx), Wq, _dev(sw), kernel=kernel)
     y, a = _host(Y), _host(acc)
     assert np.array_equal(y, _host(Y2))
     sel = np.arange(qx.shape[0]) if rows is None else np.asarray(rows)
