@@ -101,6 +101,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cold HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv", action="store_true")
+    ap.add_argument("--no-fused", action="store_true", help="skip the one-launch down_proj A/B")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the qkv_proj GEMM and the decoder-layer chain measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -477,6 +478,27 @@ def main():
     mism = float(np.mean(oracle.unpack_int4(xq_row) != oracle.unpack_int4(pk)))
 
     extra = {}
+    if not args.no_fused:
+        # The same step as one launch (spin_fwht_quant_gemm) against the two calls,
+        # both timed as whole steps on the rotating buffer sets.
+        def two(i):
+            j = i % sets
+            spin.spin_fwht_quant(X[j], HAD_N, Xq=Xq[j], x_scale=xs[j])
+            spin.spin_w4a4_gemm(Xq[j], xs[j], Wq, ws, Y=Y[j])
+
+        def one(i):
+            j = i % sets
+            spin.spin_fwht_quant_gemm(X[j], Wq, ws, Xq=Xq[j], x_scale=xs[j], Y=Y[j])
+
+        res = {"workload": "the down_proj step (fwht_quant 4096 x 12288 fp16, H_12288, INT4 + w4a4_gemm "
+                           "4096 x 4096 x 12288) as one cooperative launch against the two calls"}
+        for name, fn in (("two_calls_us", two), ("one_launch_us", one), ("two_calls_again_us", two)):
+            for i in range(args.warmup):
+                fn(i)
+            res[name] = _time(fn, args.steps, stream) * 1e3
+        res["saved_us"] = 0.5 * (res["two_calls_us"] + res["two_calls_again_us"]) - res["one_launch_us"]
+        extra["down_proj_fused"] = res
+
     if not args.no_kv:
         kv = synth.kv_config()
         Kd = [torch.from_numpy(kv["k"]).to(dev)] + [None] * (sets - 1)

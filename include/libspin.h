@@ -149,6 +149,35 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
                               const float* w_scale, int M, int N, int K, float* Y,
                               int32_t* acc_out, int kernel, void* stream);
 
+/* 32-bit words of the workspace spin_fwht_quant_gemm takes. */
+#define SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS 1025
+
+/*
+ * spin_fwht_quant_gemm — the down projection's input rotation R4 and its
+ * W4A4 product in one launch: spin_fwht_quant followed by spin_w4a4_gemm
+ * (page "SpinQuant, Reproduced", Q5: R4 is an online Hadamard right before
+ * down_proj; abstract: W4A4).
+ *
+ *   X          [M][K] float16, K == had_n == 12288 (the MLP width; H_12 (x) H_1024)
+ *   Wq, w_scale, N   the folded INT4 weights as for spin_w4a4_gemm
+ *   Xq, x_scale      OUTPUT: the codes and scales spin_fwht_quant writes
+ *   Y, acc_out       OUTPUT: as spin_w4a4_gemm writes them from those codes
+ *   workspace  SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS uint32 of device memory,
+ *              all zero before the first call; each call leaves it zero.
+ * Every output equals, bit for bit, what the two separate calls write.
+ * Requirements: x_dtype == SPIN_F16, K == had_n == 12288 (other shapes: the
+ * two calls), M, N >= 0; acc_out may be NULL.  Calls that share a workspace
+ * must not overlap (calls on one stream do not); the kernel is launched
+ * cooperatively (all its workgroups resident at once).
+ * Errors: SPIN_ERR_UNSUPPORTED for another dtype or order, SPIN_ERR_BAD_SHAPE,
+ * SPIN_ERR_NULL, SPIN_ERR_MISALIGNED as for the two calls; SPIN_ERR_HIP if
+ * the device cannot run the cooperative launch.
+ */
+spin_status spin_fwht_quant_gemm(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
+                                 const uint8_t* Wq, const float* w_scale, int N, uint8_t* Xq,
+                                 float* x_scale, float* Y, int32_t* acc_out, uint32_t* workspace,
+                                 void* stream);
+
 /*
  * spin_kv_quant — head-wise Hadamard (R3) + INT4 KV cache (page "SpinQuant,
  * Reproduced", Q5: R3 in the KV path is an online Hadamard; abstract: 4-bit

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspin.so")
-SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip", "w4a4_gemm_fp6.hip", "w4a8_gemm.hip"]
+SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip", "w4a4_gemm_fp6.hip",
+           "fwht_quant_gemm.hip", "w4a8_gemm.hip"]
 PROBE_LIB = os.path.join(PKG, "libspin_probe.so")
 PROBE_SOURCES = ["machine_probe.hip"]
 ARCH = "gfx950"

@@ -2,6 +2,7 @@
 // argument before calling these; the launchers only pick a kernel and launch.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,6 +44,11 @@ hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const u
 hipError_t launch_w4a8_gemm(const int8_t* Xq8, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, hipStream_t s);
+
+// fwht_quant (fp16, K = had_n = 12288, INT4) then the FP6 GEMM, one cooperative launch.
+hipError_t launch_fwht_quant_gemm(const __half* X, int M, int K, const uint8_t* Wq, const float* w_scale, int N,
+                                  uint8_t* Xq, float* x_scale, float* Y, int32_t* acc_out, uint32_t* workspace,
+                                  hipStream_t s);
 
 // Compute units of the current device, queried once per device and cached
 // (0 if the runtime cannot tell); safe to call from several threads.

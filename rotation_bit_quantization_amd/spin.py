@@ -18,16 +18,18 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
-           "spin_kv_qkv", "spin_w4a4_gemm_ex", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
+           "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
     SPIN_ERR_HIP = range(6)
 SPIN_F32, SPIN_F16 = 0, 1
 SPIN_GEMM_AUTO, SPIN_GEMM_INT8, SPIN_GEMM_FP6 = 0, 1, 2
+SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                     "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
+                    "spin_fwht_quant_gemm",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,13 +62,14 @@ def load():
     lib.spin_fwht_quant.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a4_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_w4a4_gemm_ex.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, i, vp]
+    lib.spin_fwht_quant_gemm.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant8.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_kv_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
     for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
-                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex"):
+                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm"):
         getattr(lib, name).restype = ctypes.c_int
     lib.spin_status_string.argtypes = [ctypes.c_int]
     lib.spin_status_string.restype = ctypes.c_char_p
@@ -182,6 +185,50 @@ def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=Fals
                                       _ptr(Y), _ptr(acc_out), int(kernel), _stream(stream))
         _raise("spin_w4a4_gemm_ex", st)
     return Y, acc_out
+
+
+_workspaces = {}
+
+
+def fused_workspace(device):
+    """The zero-initialised workspace spin_fwht_quant_gemm needs, one per device
+    (each call leaves it zero; calls sharing it must not overlap)."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros(SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS, dtype=torch.int32, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def spin_fwht_quant_gemm(X, Wq, w_scale, Xq=None, x_scale=None, Y=None, acc_out=None, want_acc=False,
+                         workspace=None, stream=None):
+    """X [M, 12288] fp16 (R4 = H_12288 applied online) and the folded Wq [N, 6144], w_scale [N]
+    -> (Y [M, N] fp32, Xq [M, 6144] u8, x_scale [M] fp32, acc [M, N] int32 or None), one launch."""
+    _check(X, "X", (torch.float16,))
+    _check(Wq, "Wq", (torch.uint8,))
+    M, K = X.shape
+    N = Wq.shape[0]
+    _check(Wq, "Wq", (torch.uint8,), (N, K // 2))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    dev = X.device
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if Xq is None else Xq
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev) if Y is None else Y
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _check(Xq, "Xq", (torch.uint8,), (M, K // 2))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    ws = fused_workspace(dev) if workspace is None else workspace
+    _check(ws, "workspace", (torch.int32,), (SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS,))
+    st = load().spin_fwht_quant_gemm(_ptr(X), SPIN_F16, M, K, K, _ptr(Wq), _ptr(w_scale), N, _ptr(Xq),
+                                     _ptr(x_scale), _ptr(Y), _ptr(acc_out), _ptr(ws), _stream(stream))
+    _raise("spin_fwht_quant_gemm", st)
+    return Y, Xq, x_scale, acc_out
 
 
 def spin_kv_quant(X, rotate, quantize=True, codes=None, scale=None, X_rot=None, want_rot=False,

@@ -190,6 +190,25 @@ def test_gemm_fp6_k_range_is_the_float32_limit():
     assert kmin == 256
 
 
+def test_fwht_quant_gemm_validation(lib):
+    f = lib.spin_fwht_quant_gemm
+
+    def call(X=A, dt=spin.SPIN_F16, M=4, K=12288, had=12288, w=A, ws_=A, N=8, xq=A, xs=A, y=A, acc=None,
+             work=A):
+        return f(X, dt, M, K, had, w, ws_, N, xq, xs, y, acc, work, None)
+
+    for name in ("X", "w", "ws_", "xq", "xs", "y", "work"):
+        assert call(**{name: None}) == spin.SPIN_ERR_NULL, name
+    assert call(dt=spin.SPIN_F32) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(had=4096) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(K=4096) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(N=-1) == spin.SPIN_ERR_BAD_SHAPE
+    for name in ("X", "w", "ws_", "xq", "xs", "y", "acc", "work"):
+        assert call(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert call(M=0) == spin.SPIN_OK
+
+
 def test_kv_qkv_validation(lib):
     f = lib.spin_kv_qkv
 
