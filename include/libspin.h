@@ -179,6 +179,25 @@ spin_status spin_fwht_quant_gemm(const void* X, spin_dtype x_dtype, int M, int K
                                  void* stream);
 
 /*
+ * spin_fwht_quant_gemm_noalloc — spin_fwht_quant_gemm for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same arguments, outputs and
+ * guarantees without the workspace: the flags live in an array of
+ * SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS words that the library holds in every
+ * GPU it runs on until the process ends (its address is looked up on the
+ * first call on each device; nothing is allocated).  The array holds the
+ * flags of up to 1024 workgroups; the kernel's grid (one workgroup per
+ * compute unit) is capped there, so no call needs more.  It is zero before
+ * the first call and every call leaves it zero.  All calls on one GPU share
+ * it: calls that overlap on one GPU race (calls on one stream do not
+ * overlap).  Errors as for spin_fwht_quant_gemm; SPIN_ERR_HIP if the array's
+ * address cannot be obtained.
+ */
+spin_status spin_fwht_quant_gemm_noalloc(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
+                                         const uint8_t* Wq, const float* w_scale, int N, uint8_t* Xq,
+                                         float* x_scale, float* Y, int32_t* acc_out, void* stream);
+
+/*
  * spin_kv_quant — head-wise Hadamard (R3) + INT4 KV cache (page "SpinQuant,
  * Reproduced", Q5: R3 in the KV path is an online Hadamard; abstract: 4-bit
  * KV cache).

@@ -72,6 +72,29 @@ spin_status kv_quant_impl(const void* X, spin_dtype x_dtype, int T, int H, int D
                                           X_rot, static_cast<hipStream_t>(stream)));
 }
 
+// spin_fwht_quant_gemm with the caller's workspace, or (workspace == NULL)
+// with the library's per-device flags, looked up only once the arguments
+// are valid and there is a product to compute.
+spin_status fwht_quant_gemm_impl(const void* X, spin_dtype x_dtype, int M, int K, int had_n, const uint8_t* Wq,
+                                 const float* w_scale, int N, uint8_t* Xq, float* x_scale, float* Y,
+                                 int32_t* acc_out, uint32_t* workspace, void* stream) {
+    if (!X || !Wq || !w_scale || !Xq || !x_scale || !Y) return SPIN_ERR_NULL;
+    if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
+    if (K != 12288 || M < 0 || N < 0) return SPIN_ERR_BAD_SHAPE;
+    const long long tiles = (static_cast<long long>(M) + 255) / 256 * ((static_cast<long long>(N) + 255) / 256);
+    if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Xq) || !aligned16(x_scale) ||
+        !aligned16(Y) || (acc_out && !aligned16(acc_out)))
+        return SPIN_ERR_MISALIGNED;
+    if (M == 0) return SPIN_OK;
+    if (N == 0)   // no product: the codes alone
+        return from_hip(spin::launch_fwht_quant(X, true, M, K, spin::HadOrder{12288, 10, true}, 4, Xq, x_scale,
+                                                nullptr, static_cast<hipStream_t>(stream)));
+    if (!workspace && spin::fwht_quant_gemm_scratch(&workspace) != hipSuccess) return SPIN_ERR_HIP;
+    return from_hip(spin::launch_fwht_quant_gemm(static_cast<const __half*>(X), M, K, Wq, w_scale, N, Xq, x_scale,
+                                                 Y, acc_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 int spin::device_cu_count() {
@@ -144,20 +167,17 @@ spin_status spin_fwht_quant_gemm(const void* X, spin_dtype x_dtype, int M, int K
                                  const uint8_t* Wq, const float* w_scale, int N, uint8_t* Xq,
                                  float* x_scale, float* Y, int32_t* acc_out, uint32_t* workspace,
                                  void* stream) {
-    if (!X || !Wq || !w_scale || !Xq || !x_scale || !Y || !workspace) return SPIN_ERR_NULL;
-    if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
-    if (K != 12288 || M < 0 || N < 0) return SPIN_ERR_BAD_SHAPE;
-    const long long tiles = (static_cast<long long>(M) + 255) / 256 * ((static_cast<long long>(N) + 255) / 256);
-    if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
-    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Xq) || !aligned16(x_scale) ||
-        !aligned16(Y) || (acc_out && !aligned16(acc_out)) || !aligned16(workspace))
-        return SPIN_ERR_MISALIGNED;
-    if (M == 0) return SPIN_OK;
-    if (N == 0)   // no product: the codes alone
-        return from_hip(spin::launch_fwht_quant(X, true, M, K, spin::HadOrder{12288, 10, true}, 4, Xq, x_scale,
-                                                nullptr, static_cast<hipStream_t>(stream)));
-    return from_hip(spin::launch_fwht_quant_gemm(static_cast<const __half*>(X), M, K, Wq, w_scale, N, Xq, x_scale,
-                                                 Y, acc_out, workspace, static_cast<hipStream_t>(stream)));
+    if (!workspace) return SPIN_ERR_NULL;
+    if (!aligned16(workspace)) return SPIN_ERR_MISALIGNED;
+    return fwht_quant_gemm_impl(X, x_dtype, M, K, had_n, Wq, w_scale, N, Xq, x_scale, Y, acc_out, workspace,
+                                stream);
+}
+
+spin_status spin_fwht_quant_gemm_noalloc(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
+                                         const uint8_t* Wq, const float* w_scale, int N, uint8_t* Xq,
+                                         float* x_scale, float* Y, int32_t* acc_out, void* stream) {
+    return fwht_quant_gemm_impl(X, x_dtype, M, K, had_n, Wq, w_scale, N, Xq, x_scale, Y, acc_out, nullptr,
+                                stream);
 }
 
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,

@@ -172,7 +172,34 @@ hipError_t launch_t(const __half* X, int M, int N, int K, const uint8_t* Wq, con
                                       dim3(kF6Threads), args, 0, s);
 }
 
+// The flags of spin_fwht_quant_gemm_noalloc: one array per device (each
+// device holds its own copy of the module's globals until the process ends),
+// zero when the module loads; every call leaves it zero again.  Host code
+// never passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint32_t scratch[SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS];
+
+constexpr int kScratchDevices = 64;
+std::atomic<uint32_t*> g_scratch[kScratchDevices];
+
 }  // namespace
+
+hipError_t fwht_quant_gemm_scratch(uint32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    uint32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<uint32_t*>(q);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 hipError_t launch_fwht_quant_gemm(const __half* X, int M, int K, const uint8_t* Wq, const float* w_scale, int N,
                                   uint8_t* Xq, float* x_scale, float* Y, int32_t* acc_out, uint32_t* workspace,

@@ -50,6 +50,11 @@ hipError_t launch_fwht_quant_gemm(const __half* X, int M, int K, const uint8_t* 
                                   uint8_t* Xq, float* x_scale, float* Y, int32_t* acc_out, uint32_t* workspace,
                                   hipStream_t s);
 
+// Device address of the current device's library-owned flags for the fused
+// kernel (SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS words, zero between calls),
+// looked up once per device.
+hipError_t fwht_quant_gemm_scratch(uint32_t** out);
+
 // Compute units of the current device, queried once per device and cached
 // (0 if the runtime cannot tell); safe to call from several threads.
 int device_cu_count();

@@ -18,7 +18,7 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
-           "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
+           "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
@@ -29,7 +29,7 @@ SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                     "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
-                    "spin_fwht_quant_gemm",
+                    "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,13 +63,15 @@ def load():
     lib.spin_w4a4_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_w4a4_gemm_ex.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, i, vp]
     lib.spin_fwht_quant_gemm.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp, vp]
+    lib.spin_fwht_quant_gemm_noalloc.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant8.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_kv_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
     for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
-                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm"):
+                 "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm",
+                 "spin_fwht_quant_gemm_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.spin_status_string.argtypes = [ctypes.c_int]
     lib.spin_status_string.restype = ctypes.c_char_p
@@ -228,6 +230,25 @@ def spin_fwht_quant_gemm(X, Wq, w_scale, Xq=None, x_scale=None, Y=None, acc_out=
     st = load().spin_fwht_quant_gemm(_ptr(X), SPIN_F16, M, K, K, _ptr(Wq), _ptr(w_scale), N, _ptr(Xq),
                                      _ptr(x_scale), _ptr(Y), _ptr(acc_out), _ptr(ws), _stream(stream))
     _raise("spin_fwht_quant_gemm", st)
+    return Y, Xq, x_scale, acc_out
+
+
+def spin_fwht_quant_gemm_noalloc(X, Wq, w_scale, Xq, x_scale, Y, acc_out=None, stream=None):
+    """spin_fwht_quant_gemm into caller-given outputs, with the library's own flags:
+    the call allocates nothing (every tensor is passed in)."""
+    _check(X, "X", (torch.float16,))
+    M, K = X.shape
+    N = Wq.shape[0]
+    _check(Wq, "Wq", (torch.uint8,), (N, K // 2))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    _check(Xq, "Xq", (torch.uint8,), (M, K // 2))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    st = load().spin_fwht_quant_gemm_noalloc(_ptr(X), SPIN_F16, M, K, K, _ptr(Wq), _ptr(w_scale), N, _ptr(Xq),
+                                             _ptr(x_scale), _ptr(Y), _ptr(acc_out), _stream(stream))
+    _raise("spin_fwht_quant_gemm_noalloc", st)
     return Y, Xq, x_scale, acc_out
 
 

@@ -209,6 +209,25 @@ def test_fwht_quant_gemm_validation(lib):
     assert call(M=0) == spin.SPIN_OK
 
 
+def test_fwht_quant_gemm_noalloc_validation(lib):
+    """The allocation-free variant validates like the workspace one, before it
+    touches its per-device flags (so no GPU is needed for these)."""
+    f = lib.spin_fwht_quant_gemm_noalloc
+
+    def call(X=A, dt=spin.SPIN_F16, M=4, K=12288, had=12288, w=A, ws_=A, N=8, xq=A, xs=A, y=A, acc=None):
+        return f(X, dt, M, K, had, w, ws_, N, xq, xs, y, acc, None)
+
+    for name in ("X", "w", "ws_", "xq", "xs", "y"):
+        assert call(**{name: None}) == spin.SPIN_ERR_NULL, name
+    assert call(dt=spin.SPIN_F32) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(had=4096) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(K=4096) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    for name in ("X", "w", "ws_", "xq", "xs", "y", "acc"):
+        assert call(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert call(M=0) == spin.SPIN_OK
+
+
 def test_kv_qkv_validation(lib):
     f = lib.spin_kv_qkv
 
