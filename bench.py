@@ -102,6 +102,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv", action="store_true")
     ap.add_argument("--no-fused", action="store_true", help="skip the one-launch down_proj A/B")
+    ap.add_argument("--no-f6", action="store_true", help="skip the FP6-operand-layout step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the qkv_proj GEMM and the decoder-layer chain measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -478,6 +479,40 @@ def main():
     mism = float(np.mean(oracle.unpack_int4(xq_row) != oracle.unpack_int4(pk)))
 
     extra = {}
+    if not args.no_f6:
+        # The same step with the activation codes in the FP6 operand layout
+        # (spin_fwht_quant_f6 + spin_w4a4_gemm_f6), same buffers rotating.
+        Xf6 = [torch.empty((spin.f6_bytes(M, K),), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        xsum = [torch.empty((M,), dtype=torch.int32, device=dev) for _ in range(sets)]
+
+        def step6(i, ev=None):
+            j = i % sets
+            if ev is not None:
+                he.record(ev[0], stream)
+            spin.spin_fwht_quant_f6(X[j], Xf6=Xf6[j], x_sum=xsum[j], x_scale=xs[j])
+            if ev is not None:
+                he.record(ev[1], stream)
+            spin.spin_w4a4_gemm_f6(Xf6[j], xsum[j], xs[j], Wq, ws, Y=Y[j])
+            if ev is not None:
+                he.record(ev[2], stream)
+
+        for i in range(args.warmup):
+            step6(i)
+        torch.cuda.synchronize()
+        ev6 = [[he.new() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step6(i, ev6[i])
+        torch.cuda.synchronize()
+        f6_us = float(np.mean([he.ms(e[0], e[1]) for e in ev6])) * 1e3
+        g6_us = float(np.mean([he.ms(e[1], e[2]) for e in ev6])) * 1e3
+        he.release()
+        extra["down_proj_f6"] = {
+            "workload": "the down_proj step with the activation codes in the FP6 operand layout: "
+                        "spin_fwht_quant_f6 (4096 x 12288 fp16, H_12288) + spin_w4a4_gemm_f6 (4096 x 4096 x 12288)",
+            "fwht_quant_f6_us": f6_us, "gemm_f6_us": g6_us, "gemm_f6_tops": gemm_ops / g6_us / 1e6,
+            "step_us": f6_us + g6_us}
+        del Xf6, xsum
+
     if not args.no_fused:
         # The same step as one launch (spin_fwht_quant_gemm) against the two calls,
         # both timed as whole steps on the rotating buffer sets.

@@ -149,6 +149,51 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
                               const float* w_scale, int M, int N, int K, float* Y,
                               int32_t* acc_out, int kernel, void* stream);
 
+/*
+ * The FP6 operand layout of activation codes, written by spin_fwht_quant_f6
+ * and read by spin_w4a4_gemm_f6 (this library's format; the pages fix no
+ * storage): the INT4 codes q of an [M][K] activation matrix, each held as the
+ * 6-bit field of u = q + 8 (bits 0..3 = u, bits 4..5 = 0: the FP6 E2M3 value
+ * u / 8), ordered for the gfx950 matrix cores.  Row r, code k lies in the
+ * 1536-byte region (r / 32) * (K / 64) + k / 64, at byte
+ * ((k % 64) / 32) * 768 + (r % 32) * 24 + ((k % 32) / 16) * 12 of it, in field
+ * sigma(k % 16) of those 12 bytes read as a 96-bit little-endian number (field
+ * p at bits 6p .. 6p + 5), sigma = 0 1 12 2 3 14 4 5 11 6 7 13 8 9 15 10.
+ * Rows are rounded up to a multiple of 32 (rows past M are never read into a
+ * result); K % 64 == 0.  1.5 bytes per code.
+ */
+#define SPIN_F6_BYTES(M, K) ((size_t)(((M) + 31) / 32) * ((size_t)(K) / 64) * 1536)
+
+/*
+ * spin_fwht_quant_f6 — spin_fwht_quant (per-token INT4 after the R4 Hadamard,
+ * page "SpinQuant, Reproduced", Q5) with the codes written in the FP6
+ * operand layout above, for spin_w4a4_gemm_f6.
+ *
+ *   X        [M][K] float16, K == had_n == 12288
+ *   Xf6      SPIN_F6_BYTES(M, K) bytes   OUTPUT: the codes spin_fwht_quant
+ *            computes, in the FP6 operand layout
+ *   x_sum    [M] int32     OUTPUT: sum_k q[m][k]
+ *   x_scale  [M] float32   OUTPUT: as spin_fwht_quant
+ * Requirements: x_dtype == SPIN_F16, K == had_n == 12288, M >= 0.
+ */
+spin_status spin_fwht_quant_f6(const void* X, spin_dtype x_dtype, int M, int K, int had_n, uint8_t* Xf6,
+                               int32_t* x_sum, float* x_scale, void* stream);
+
+/*
+ * spin_w4a4_gemm_f6 — spin_w4a4_gemm with the activation codes in the FP6
+ * operand layout (abstract: W4A4): Y and acc_out are the same bits
+ * spin_w4a4_gemm gives for those codes.
+ *
+ *   Xf6      SPIN_F6_BYTES(M, K) bytes (from spin_fwht_quant_f6)
+ *   x_sum    [M] int32, sum_k q[m][k]   x_scale [M] float32
+ *   Wq, w_scale, Y, acc_out   as for spin_w4a4_gemm
+ * Requirements: M, N >= 0, K % 128 == 0,
+ * SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K.
+ */
+spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
+                              const uint8_t* Wq, const float* w_scale, int M, int N, int K, float* Y,
+                              int32_t* acc_out, void* stream);
+
 /* 32-bit words of the workspace spin_fwht_quant_gemm takes. */
 #define SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS 1025
 

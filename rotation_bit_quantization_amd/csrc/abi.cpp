@@ -180,6 +180,33 @@ spin_status spin_fwht_quant_gemm_noalloc(const void* X, spin_dtype x_dtype, int 
                                 stream);
 }
 
+spin_status spin_fwht_quant_f6(const void* X, spin_dtype x_dtype, int M, int K, int had_n, uint8_t* Xf6,
+                               int32_t* x_sum, float* x_scale, void* stream) {
+    if (!X || !Xf6 || !x_sum || !x_scale) return SPIN_ERR_NULL;
+    if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
+    if (K != 12288 || M < 0) return SPIN_ERR_BAD_SHAPE;
+    if (!aligned16(X) || !aligned16(Xf6) || !aligned16(x_sum) || !aligned16(x_scale)) return SPIN_ERR_MISALIGNED;
+    if (M == 0) return SPIN_OK;
+    return from_hip(spin::launch_fwht_quant_f6(static_cast<const __half*>(X), M, Xf6, x_sum, x_scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
+                              const uint8_t* Wq, const float* w_scale, int M, int N, int K, float* Y,
+                              int32_t* acc_out, void* stream) {
+    if (!Xf6 || !x_sum || !x_scale || !Wq || !w_scale || !Y) return SPIN_ERR_NULL;
+    if (M < 0 || N < 0 || K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_GEMM_FP6_MAX_K)
+        return SPIN_ERR_BAD_SHAPE;
+    const long long tiles = (static_cast<long long>(M) + 255) / 256 * ((static_cast<long long>(N) + 255) / 256);
+    if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
+    if (!aligned16(Xf6) || !aligned16(x_sum) || !aligned16(x_scale) || !aligned16(Wq) || !aligned16(w_scale) ||
+        !aligned16(Y) || (acc_out && !aligned16(acc_out)))
+        return SPIN_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return SPIN_OK;
+    return from_hip(spin::launch_w4a4_gemm_f6(Xf6, x_sum, x_scale, Wq, w_scale, M, N, K, Y, acc_out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
                           uint8_t* codes, uint16_t* scale, float* X_rot, void* stream) {
     return kv_quant_impl(X, x_dtype, T, H, D, rotate, 4, codes, scale, X_rot, stream);

@@ -224,30 +224,36 @@ __device__ __forceinline__ float wave_max64(float v) {
     return __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
+// Sixteen consecutive INT4 codes from the magic-number quantizer (exact
+// quotient near a tie or outside the fast range) as two dwords of nibbles.
+__device__ __forceinline__ uint2 quant16_nibbles(const f16v& u, float cr, float nrm, float s, bool fast) {
+    uint32_t w0 = 0, w1 = 0;
+    bool exact = !fast;
+    if (fast) {
+        uint32_t f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuantMagic));
+        w0 = pack8_magic(f);
+        w1 = pack8_magic(f + 8);
+        exact = any_near_tie(f) | any_near_tie(f + 8);   // no short circuit: one branch
+    }
+    if (exact) {
+        int c[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) c[k] = quant_exact(u[k] * nrm, s);
+        w0 = pack8(c);
+        w1 = pack8(c + 8);
+    }
+    return make_uint2(w0, w1);
+}
+
 // Sixteen consecutive codes from the magic-number quantizer (exact quotient
 // near a tie or outside the fast range), one store.
 template <int BITS>
 __device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float cr, float nrm, float s,
                                               bool fast) {
     if (BITS == 4) {
-        uint32_t w0 = 0, w1 = 0;
-        bool exact = !fast;
-        if (fast) {
-            uint32_t f[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuantMagic));
-            w0 = pack8_magic(f);
-            w1 = pack8_magic(f + 8);
-            exact = any_near_tie(f) | any_near_tie(f + 8);   // no short circuit: one branch
-        }
-        if (exact) {
-            int c[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) c[k] = quant_exact(u[k] * nrm, s);
-            w0 = pack8(c);
-            w1 = pack8(c + 8);
-        }
-        *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(p) = quant16_nibbles(u, cr, nrm, s, fast);
     } else {
         uint4 w = make_uint4(0, 0, 0, 0);
         bool exact = !fast;
@@ -268,14 +274,12 @@ __device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float c
     }
 }
 
-// One row by one wave (`lane` = the thread's index in its wave): codes of row
-// `row` to Xq, its scale to x_scale[row], the rotated values to X_rot when
-// WRITE_ROT.
-template <int BITS, bool WRITE_ROT>
-__device__ __forceinline__ void fwht12288_row(const __half* __restrict__ X, size_t row, int lane, float norm,
-                                              float mone,
-                                              uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
-                                              float* __restrict__ X_rot) {
+// The transform of one row by one wave (`lane` = the thread's index in its
+// wave): u[a] * nrm are the lane's sixteen values y[1024 a + 32 c + 16 h .. + 15]
+// (lane = 32 h + c); returns the row's scale fl32(max |y| / qmax).
+template <int BITS>
+__device__ __forceinline__ float fwht12288_transform(const __half* __restrict__ X, size_t row, int lane,
+                                                     float norm, float mone, f16v (&u)[12], float& nrm) {
     const int h = lane >> 5, c = lane & 31;
     const __half* xr = X + row * 12288 + 32 * c + 16 * h;
     u4v raw[12][2];
@@ -286,8 +290,7 @@ __device__ __forceinline__ void fwht12288_row(const __half* __restrict__ X, size
     }
     u4v sa, sb;
     operand_signs(lane, sa, sb);
-    f16v u[12];
-    float nrm = norm * 32.0f;
+    nrm = norm * 32.0f;
     transform_row12288(raw, 0x28002800u, sa, sb, mone, u);     // +-2^-5
     float amax = wave_max64(row_absmax(u)) * nrm;       // = max_i fl32(|u_i| * nrm)
     if (!(amax >= 2.0f)) {
@@ -313,7 +316,19 @@ __device__ __forceinline__ void fwht12288_row(const __half* __restrict__ X, size
         transform_row12288(raw2, mag * 0x10001u, sa, sb, mone, u);
         amax = wave_max64(row_absmax(u)) * nrm;
     }
-    const float s = __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
+    return __fdiv_rn(amax, BITS == 4 ? kSeven : kQmax8);
+}
+
+// One row by one wave: codes of row `row` to Xq, its scale to x_scale[row],
+// the rotated values to X_rot when WRITE_ROT.
+template <int BITS, bool WRITE_ROT>
+__device__ __forceinline__ void fwht12288_row(const __half* __restrict__ X, size_t row, int lane, float norm,
+                                              float mone, uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
+                                              float* __restrict__ X_rot) {
+    const int h = lane >> 5, c = lane & 31;
+    f16v u[12];
+    float nrm;
+    const float s = fwht12288_transform<BITS>(X, row, lane, norm, mone, u, nrm);
     if (lane == 0) x_scale[row] = s;
     const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
     const float cr = fast ? nrm * __fdiv_rn(1.0f, s) : 0.0f;
@@ -331,6 +346,38 @@ __device__ __forceinline__ void fwht12288_row(const __half* __restrict__ X, size
                     make_float4(u[a][4 * q] * nrm, u[a][4 * q + 1] * nrm, u[a][4 * q + 2] * nrm,
                                 u[a][4 * q + 3] * nrm);
     }
+}
+
+
+// One row by one wave with the codes written in the FP6 operand layout of
+// spin_fwht_quant_f6 (row block of 32 rows, 64-code k-step: a 1536-byte
+// region [k-half][row][24 bytes]; lane 32 h + c holds codes 32 c + 16 h ..
+// + 15 of every 1024-block a, i.e. half-group h of k-half c % 2 of k-step
+// 16 a + c / 2) and the sum of the row's codes to x_sum[row].
+__device__ __forceinline__ void fwht12288_row_f6(const __half* __restrict__ X, size_t row, int lane, float norm,
+                                                 float mone, uint8_t* __restrict__ Xf6,
+                                                 int32_t* __restrict__ x_sum, float* __restrict__ x_scale) {
+    const int h = lane >> 5, c = lane & 31;
+    f16v u[12];
+    float nrm;
+    const float s = fwht12288_transform<4>(X, row, lane, norm, mone, u, nrm);
+    if (lane == 0) x_scale[row] = s;
+    const bool fast = (s >= 0x1p-100f) && (s <= 0x1p+100f);
+    const float cr = fast ? nrm * __fdiv_rn(1.0f, s) : 0.0f;
+    uint8_t* out = Xf6 + ((row >> 5) * (12288 / 64) + (c >> 1)) * 1536 + (c & 1) * 768 + (row & 31) * 24 + h * 12;
+    int sum = 0;
+#pragma unroll
+    for (int a = 0; a < 12; ++a) {
+        const uint2 w = quant16_nibbles(u[a], cr, nrm, s, fast);
+        sum = __builtin_amdgcn_sdot8(static_cast<int>(w.x), 0x11111111, sum, false);
+        sum = __builtin_amdgcn_sdot8(static_cast<int>(w.y), 0x11111111, sum, false);
+        uint32_t o[3];
+        spread16(w.x ^ 0x88888888u, w.y ^ 0x88888888u, o);
+        *reinterpret_cast<uint3*>(out + a * 16 * 1536) = make_uint3(o[0], o[1], o[2]);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
+    if (lane == 0) x_sum[row] = sum;
 }
 
 }  // namespace spin

@@ -99,6 +99,18 @@ __global__ __launch_bounds__(kRowThreads) void fwht_quant_rowlds(
         for (int i = tid; i < K; i += kRowThreads) yr[i] = row[i];
     }
 }
+// The FP6-layout producer: one wave (workgroup of 64) per row, rows mapped to
+// workgroups so that each XCD (workgroups b with the same b % 8) owns whole
+// 32-row blocks: the rows of a 1536-byte region are written through one L2.
+__global__ __launch_bounds__(64, 2) void fwht_quant_k12288_f6(const __half* __restrict__ X, float norm, float mone,
+                                                              int M, int rows_per_xcd, uint8_t* __restrict__ Xf6,
+                                                              int32_t* __restrict__ x_sum,
+                                                              float* __restrict__ x_scale) {
+    const int row = static_cast<int>(blockIdx.x % 8) * rows_per_xcd + static_cast<int>(blockIdx.x / 8);
+    if (row >= M) return;
+    fwht12288_row_f6(X, static_cast<size_t>(row), threadIdx.x, norm, mone, Xf6, x_sum, x_scale);
+}
+
 // One wave (workgroup of 64) per row.
 template <int BITS, bool WRITE_ROT>
 __global__ __launch_bounds__(64, 2) void fwht_quant_k12288_mfma(
@@ -395,6 +407,15 @@ hipError_t launch_fwht_quant(const void* X, bool x_f16, int M, int K, HadOrder h
                              float* x_scale, float* X_rot, hipStream_t s) {
     return bits == 8 ? launch_fwht_quant_bits<8>(X, x_f16, M, K, h, Xq, x_scale, X_rot, s)
                      : launch_fwht_quant_bits<4>(X, x_f16, M, K, h, Xq, x_scale, X_rot, s);
+}
+
+hipError_t launch_fwht_quant_f6(const __half* X, int M, uint8_t* Xf6, int32_t* x_sum, float* x_scale,
+                                hipStream_t s) {
+    const int rows_per_xcd = (M + 8 * 32 - 1) / (8 * 32) * 32;
+    const float norm = static_cast<float>(1.0 / __builtin_sqrt(12288.0));
+    hipLaunchKernelGGL(fwht_quant_k12288_f6, dim3(static_cast<unsigned>(8 * rows_per_xcd)), dim3(64), 0, s, X, norm,
+                       -1.0f, M, rows_per_xcd, Xf6, x_sum, x_scale);
+    return hipGetLastError();
 }
 
 }  // namespace spin

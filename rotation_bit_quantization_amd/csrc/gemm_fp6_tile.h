@@ -95,13 +95,6 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Sixteen offset nibbles (two dwords) -> sixteen 6-bit fields (three dwords).
-__device__ __forceinline__ void spread16(uint32_t a, uint32_t b, uint32_t* o) {
-    o[0] = (a & 0x0F00F00Fu) | ((a & 0x300F00F0u) << 2);
-    o[1] = (b & 0xF00F00F0u) | __builtin_amdgcn_alignbit(b & 0x00F00F00u, a, 30);
-    o[2] = (a & 0x00F00F00u) | ((b & 0x0F00F00Fu) << 2);
-}
-
 // One 16-byte chunk of packed codes -> six dwords of FP6 fields (u = q + 8),
 // and the sum of its 32 codes added to `sum`.
 __device__ __forceinline__ void chunk_to_fp6(uint4 q, uint32_t* o, int& sum) {
@@ -346,6 +339,226 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
                 const int col = n0 + ct;
                 if (col < N) {
                     const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa + sums[kF6T + ct]) - k64;
+                    float y = static_cast<float>(a) * sx;
+                    y = y * w_scale[col];
+                    Y[static_cast<size_t>(row) * N + col] = y;
+                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_tile_f6a: the same tile with the activation codes already in the FP6
+// operand layout of spin_fwht_quant_f6 (u = q + 8 fields, one 1536-byte
+// region per 32 rows and 64-code k-step, a row block's k-steps adjacent) and
+// their row sums given.  The A part of a stage is then eight contiguous 3 KB
+// pieces that each wave copies global -> LDS with the LDS DMA (no registers,
+// no ALU); only the weight codes are converted, and only their sums are
+// formed.  Stage layout (both halves alike): [block of 32 rows][k-step]
+// [k-half][row][24 bytes], A at 0 and B at kF6F6aHalf.
+constexpr int kF6F6aBlock = 2 * 2 * kF6Region;               // 3 KB: two k-steps x two k-halves
+constexpr int kF6F6aHalf = 8 * kF6F6aBlock;                  // 24 KB
+static_assert(2 * kF6F6aHalf == kF6StageBytes, "same stage size as the nibble-input tile");
+
+template <bool WRITE_ACC>
+__device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, const int32_t* __restrict__ x_sum,
+                                              const float* __restrict__ x_scale, const uint8_t* __restrict__ Wq,
+                                              const float* __restrict__ w_scale, int M, int N, int K,
+                                              float* __restrict__ Y, int32_t* __restrict__ acc_out, int tm, int tn,
+                                              uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m0 = tm * kF6T, n0 = tn * kF6T;
+    const size_t rowBytes = static_cast<size_t>(K) / 2;
+    const int steps = K / kF6StepCodes;
+    const int ksteps = K / 64;
+    const uint32_t lds0 = lds_addr(lds);
+
+    // A: wave w copies row block m0 / 32 + w (the last block for tiles past M)
+    const int rb = min(m0 / 32 + wave, (M + 31) / 32 - 1);
+    const uint8_t* srcA = Xf6 + static_cast<size_t>(rb) * ksteps * 1536 + lane * 16;
+    const uint32_t dmaA = lds0 + wave * kF6F6aBlock;          // wave-uniform
+    auto dma = [&](int step, uint32_t stage_off) {
+        const uint8_t* p = srcA + static_cast<size_t>(step) * 2 * 1536;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            lds_dma16(p + q * 1024, __builtin_amdgcn_readfirstlane(dmaA + stage_off + q * 1024));
+    };
+    // B: thread (w, l) converts k-half l / 32 of both k-steps of weight row
+    // 32 w + l % 32: two 16-byte chunks per step, loaded one step ahead.
+    const int r = 32 * wave + (lane & 31);
+    const int h = lane >> 5;
+    const uint32_t offB = static_cast<uint32_t>(min(r, N - n0 - 1)) * static_cast<uint32_t>(rowBytes) + 16u * h;
+    const uint8_t* baseB = Wq + static_cast<size_t>(n0) * rowBytes;
+    const uint32_t dstB = kF6F6aHalf + wave * kF6F6aBlock + h * kF6Region + (lane & 31) * 24;
+    int sumB = 0;
+
+    const int wm = wave >> 2, wn = wave & 3;
+    const uint32_t fr = lds0 + (lane >> 5) * kF6Region + (lane & 31) * 24;
+    uint32_t fbase[6];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fbase[i] = opaque(fr + (4 * wm + i) * kF6F6aBlock);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fbase[4 + j] = opaque(fr + kF6F6aHalf + (2 * wn + j) * kF6F6aBlock);
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    typedef const __attribute__((address_space(3))) uint64_t* lds_u64;
+    auto frag = [&](uint32_t off, int f) {
+        const lds_u64 a = reinterpret_cast<lds_u64>(static_cast<uintptr_t>(fbase[f] + off));
+        const uint64_t x = a[0], y = a[1], z = a[2];
+        const int u = __builtin_nondeterministic_value(0);   // the operand reads six dwords
+        return v8i{static_cast<int>(x), static_cast<int>(x >> 32), static_cast<int>(y), static_cast<int>(y >> 32),
+                   static_cast<int>(z), static_cast<int>(z >> 32), u, u};
+    };
+    auto load_b = [&](int step, uint4* p) {
+        const size_t o = static_cast<size_t>(step) * kF6StepBytes;
+        p[0] = *reinterpret_cast<const uint4*>(baseB + o + offB);
+        p[1] = *reinterpret_cast<const uint4*>(baseB + o + 32 + offB);
+    };
+    auto put = [&](uint8_t* d, const uint32_t* o) {
+        uint2* q = reinterpret_cast<uint2*>(d);
+        q[0] = make_uint2(o[0], o[1]);
+        q[1] = make_uint2(o[2], o[3]);
+        q[2] = make_uint2(o[4], o[5]);
+    };
+    auto convert_b = [&](uint32_t stage_off, const uint4* p) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t o[6];
+            chunk_to_fp6(p[ks], o, sumB);
+            put(lds + stage_off + dstB + ks * 2 * kF6Region, o);
+        }
+    };
+    v8i fa[4], fbx[2], fby[2];
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    // One step s, as in gemm_tile, with
+    //   * CONV: the weight codes of step s + 2 (registers p_conv) converted
+    //     into stage `dst`, half a chunk after the first and third MFMA pairs
+    //     of each k-step; before anything else the step waits for all of
+    //     p_conv, then copies step s + 2's activation block into `dst` and
+    //     loads step s + 3's weight chunks into p_load, in that order, so
+    //     that the compiler's waits for those loads never include a copy
+    //     issued after them; the copy is waited for before the barrier;
+    //   * the operand reads of the next k-step during the current MFMAs.
+    auto body = [&](int s, uint32_t cur, uint32_t nxt, uint32_t dst, const uint4* p_conv, uint4* p_load,
+                    bool conv, bool prefetch) {
+        if (conv) {
+            asm volatile("" ::"v"(p_conv[0].x), "v"(p_conv[0].y), "v"(p_conv[0].z), "v"(p_conv[0].w),
+                         "v"(p_conv[1].x), "v"(p_conv[1].y), "v"(p_conv[1].z), "v"(p_conv[1].w));
+            dma(s + 2, dst);
+            load_b(min(s + 3, steps - 1), p_load);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            v8i* fb = ks == 0 ? fbx : fby;
+            v8i* fbn = ks == 0 ? fby : fbx;
+            const uint32_t noff = ks == 0 ? cur + kF6Region * 2 : nxt;
+            const bool more = ks == 0 || prefetch;
+            if (more) {
+                fbn[0] = frag(noff, 4);
+                fbn[1] = frag(noff, 5);
+            }
+            fence();
+            uint32_t o[6];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[0], acc[i][0], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[1], acc[i][1], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                if (more) fa[i] = frag(noff, i);
+                if (conv && (i & 1) == 0) {
+                    const int half = i >> 1;
+                    const uint4 q = p_conv[ks];
+                    const uint32_t a = half ? q.z : q.x, b = half ? q.w : q.y;
+                    sumB = __builtin_amdgcn_sdot8(static_cast<int>(a), 0x11111111, sumB, false);
+                    sumB = __builtin_amdgcn_sdot8(static_cast<int>(b), 0x11111111, sumB, false);
+                    spread16(a ^ 0x88888888u, b ^ 0x88888888u, o + 3 * half);
+                    pin3(o + 3 * half);
+                    if (half) put(lds + dst + dstB + ks * 2 * kF6Region, o);
+                }
+                fence();
+            }
+        }
+        if (conv) SPIN_WAIT_VMCNT(2);   // this step's copies; the two weight loads may stay in flight
+        barrier_lds();
+    };
+
+    // prologue: steps 0 and 1 into stages 0 and 1, step 2's weights in
+    // registers, the operands of step 0's first k-step read
+    uint4 P0[2], P1[2];
+    dma(0, 0);
+    dma(min(1, steps - 1), kF6StageBytes);
+    load_b(0, P0);
+    load_b(min(1, steps - 1), P1);
+    convert_b(0, P0);
+    load_b(min(2, steps - 1), P0);
+    convert_b(kF6StageBytes, P1);
+    SPIN_WAIT_VMCNT(2);            // the copies; step 2's weight loads may stay in flight
+    barrier_lds();
+    fbx[0] = frag(0, 4);
+    fbx[1] = frag(0, 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(0, i);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every body starts with no LDS access in flight
+
+    uint32_t cur = 0, nxt = kF6StageBytes, dst = 2 * kF6StageBytes;
+    auto rotate = [&] {
+        const uint32_t t = cur;
+        cur = nxt;
+        nxt = dst;
+        dst = t;
+    };
+    int s = 0;
+    for (; s + 3 < steps; s += 2) {
+        body(s, cur, nxt, dst, P0, P1, true, true);
+        rotate();
+        body(s + 1, cur, nxt, dst, P1, P0, true, true);
+        rotate();
+    }
+    if (s + 2 < steps) {
+        body(s, cur, nxt, dst, P0, P1, true, true);
+        rotate();
+        ++s;
+    }
+    body(s, cur, nxt, dst, P0, P1, false, true);
+    rotate();
+    body(s + 1, cur, nxt, dst, P0, P1, false, false);
+
+    // weight-code sums per column (the two halves of a row sit in lanes l and
+    // l + 32), through the first stage, idle after the last barrier
+    sumB += __shfl_xor(sumB, 32, 64);
+    int* sums = reinterpret_cast<int*>(lds);
+    if (h == 0) sums[r] = sumB;
+    barrier_lds();
+
+    // epilogue as in gemm_tile, the activation sums from x_sum
+    const int k64 = 64 * K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int rt = 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const int row = m0 + rt;
+            if (row >= M) continue;
+            const float sx = x_scale[row];
+            const int sa = x_sum[row];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int ct = 64 * wn + 32 * j + (lane & 31);
+                const int col = n0 + ct;
+                if (col < N) {
+                    const int a = static_cast<int>(acc[i][j][rr]) - 8 * (sa + sums[ct]) - k64;
                     float y = static_cast<float>(a) * sx;
                     y = y * w_scale[col];
                     Y[static_cast<size_t>(row) * N + col] = y;

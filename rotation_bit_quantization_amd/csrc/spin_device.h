@@ -297,4 +297,16 @@ __device__ __forceinline__ bool any_near_tie8(const uint32_t* f) {
     return min(min(m01, m23), min(m45, m67)) < 5u;
 }
 
+// FP6 operand fields.  Sixteen offset nibbles u = q + 8 (two dwords, nibble
+// k at bits 4k of a:b) -> sixteen 6-bit fields (three dwords): nibble k goes
+// to field sigma(k) (bits 6 sigma(k) .. + 5 of o[0]:o[1]:o[2]) with
+// sigma = 0 1 12 2 3 14 4 5 11 6 7 13 8 9 15 10, its four bits in the field's
+// low bits and the top two bits zero, so that the field is the FP6 E2M3
+// value u / 8.  Nine mask / shift / funnel-shift instructions.
+__device__ __forceinline__ void spread16(uint32_t a, uint32_t b, uint32_t* o) {
+    o[0] = (a & 0x0F00F00Fu) | ((a & 0x300F00F0u) << 2);
+    o[1] = (b & 0xF00F00F0u) | __builtin_amdgcn_alignbit(b & 0x00F00F00u, a, 30);
+    o[2] = (a & 0x00F00F00u) | ((b & 0x0F00F00Fu) << 2);
+}
+
 }  // namespace spin

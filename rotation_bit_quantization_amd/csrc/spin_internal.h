@@ -55,6 +55,14 @@ hipError_t launch_fwht_quant_gemm(const __half* X, int M, int K, const uint8_t* 
 // looked up once per device.
 hipError_t fwht_quant_gemm_scratch(uint32_t** out);
 
+// fp16 rows of 12288, H_12 (x) H_1024, INT4 codes in the FP6 operand layout + row code sums.
+hipError_t launch_fwht_quant_f6(const __half* X, int M, uint8_t* Xf6, int32_t* x_sum, float* x_scale,
+                                hipStream_t s);
+// The FP6 GEMM on activation codes in that layout.
+hipError_t launch_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale, const uint8_t* Wq,
+                               const float* w_scale, int M, int N, int K, float* Y, int32_t* acc_out,
+                               hipStream_t s);
+
 // Compute units of the current device, queried once per device and cached
 // (0 if the runtime cannot tell); safe to call from several threads.
 int device_cu_count();

@@ -21,6 +21,17 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6(
     gemm_tile<WRITE_ACC>(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, tm, tn, lds);
 }
 
+template <bool WRITE_ACC>
+__global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6a(
+    const uint8_t* __restrict__ Xf6, const int32_t* __restrict__ x_sum, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kF6StageBytes];
+    int tm, tn;
+    tile_of(blockIdx.x, (M + kF6T - 1) / kF6T, (N + kF6T - 1) / kF6T, &tm, &tn);
+    gemm_tile_f6a<WRITE_ACC>(Xf6, x_sum, x_scale, Wq, w_scale, M, N, K, Y, acc_out, tm, tn, lds);
+}
+
 }  // namespace
 
 // Measured on MI355X against the int8 kernels (random codes, µs):
@@ -58,6 +69,21 @@ hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const u
     else
         hipLaunchKernelGGL((w4a4_gemm_fp6<false>), grid, dim3(kF6Threads), 0, s, Xq, x_scale, Wq, w_scale, M,
                            N, K, Y, acc_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale, const uint8_t* Wq,
+                               const float* w_scale, int M, int N, int K, float* Y, int32_t* acc_out,
+                               hipStream_t s) {
+    if (K % kF6StepCodes != 0 || K < 2 * kF6StepCodes || K > kGemmFp6MaxK) return hipErrorInvalidValue;
+    const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
+    const dim3 grid(static_cast<unsigned>(tiles));
+    if (acc_out)
+        hipLaunchKernelGGL((w4a4_gemm_fp6_f6a<true>), grid, dim3(kF6Threads), 0, s, Xf6, x_sum, x_scale, Wq,
+                           w_scale, M, N, K, Y, acc_out);
+    else
+        hipLaunchKernelGGL((w4a4_gemm_fp6_f6a<false>), grid, dim3(kF6Threads), 0, s, Xf6, x_sum, x_scale, Wq,
+                           w_scale, M, N, K, Y, acc_out);
     return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_ERR_BAD_SHAPE", "SPIN_ERR_MISALIGNED", "SPIN_ERR_UNSUPPORTED", "SPIN_ERR_HIP",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
-           "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
+           "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6", "spin_w4a4_gemm_f6",
+           "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
@@ -29,7 +30,8 @@ SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                     "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
-                    "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc",
+                    "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6",
+                    "spin_w4a4_gemm_f6",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +66,8 @@ def load():
     lib.spin_w4a4_gemm_ex.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, i, vp]
     lib.spin_fwht_quant_gemm.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp, vp]
     lib.spin_fwht_quant_gemm_noalloc.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp]
+    lib.spin_fwht_quant_f6.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+    lib.spin_w4a4_gemm_f6.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
@@ -71,7 +75,7 @@ def load():
     lib.spin_kv_qkv.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
     for name in ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                  "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm",
-                 "spin_fwht_quant_gemm_noalloc"):
+                 "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6", "spin_w4a4_gemm_f6"):
         getattr(lib, name).restype = ctypes.c_int
     lib.spin_status_string.argtypes = [ctypes.c_int]
     lib.spin_status_string.restype = ctypes.c_char_p
@@ -186,6 +190,52 @@ def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=Fals
         st = load().spin_w4a4_gemm_ex(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, 2 * Kh,
                                       _ptr(Y), _ptr(acc_out), int(kernel), _stream(stream))
         _raise("spin_w4a4_gemm_ex", st)
+    return Y, acc_out
+
+
+def f6_bytes(M, K):
+    """Bytes of an [M][K] activation code matrix in the FP6 operand layout."""
+    return ((M + 31) // 32) * (K // 64) * 1536
+
+
+def spin_fwht_quant_f6(X, Xf6=None, x_sum=None, x_scale=None, stream=None):
+    """X [M, 12288] fp16 -> (Xf6 uint8 [f6_bytes(M, 12288)], x_sum [M] int32, x_scale [M] fp32)."""
+    _check(X, "X", (torch.float16,))
+    M, K = X.shape
+    dev = X.device
+    Xf6 = torch.empty((f6_bytes(M, K),), dtype=torch.uint8, device=dev) if Xf6 is None else Xf6
+    x_sum = torch.empty((M,), dtype=torch.int32, device=dev) if x_sum is None else x_sum
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    _check(Xf6, "Xf6", (torch.uint8,), (f6_bytes(M, K),))
+    _check(x_sum, "x_sum", (torch.int32,), (M,))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    st = load().spin_fwht_quant_f6(_ptr(X), SPIN_F16, M, K, K, _ptr(Xf6), _ptr(x_sum), _ptr(x_scale),
+                                   _stream(stream))
+    _raise("spin_fwht_quant_f6", st)
+    return Xf6, x_sum, x_scale
+
+
+def spin_w4a4_gemm_f6(Xf6, x_sum, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=False, stream=None):
+    """Activation codes in the FP6 operand layout (+ row sums, scales) x packed Wq [N, K/2]
+    -> (Y [M, N] fp32, acc [M, N] int32 or None)."""
+    _check(x_sum, "x_sum", (torch.int32,))
+    M = x_sum.shape[0]
+    _check(Wq, "Wq", (torch.uint8,))
+    N, Kh = Wq.shape
+    K = 2 * Kh
+    _check(Xf6, "Xf6", (torch.uint8,), (f6_bytes(M, K),))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    dev = Wq.device
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev) if Y is None else Y
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    st = load().spin_w4a4_gemm_f6(_ptr(Xf6), _ptr(x_sum), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K,
+                                  _ptr(Y), _ptr(acc_out), _stream(stream))
+    _raise("spin_w4a4_gemm_f6", st)
     return Y, acc_out
 
 

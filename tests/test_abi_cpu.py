@@ -228,6 +228,37 @@ def test_fwht_quant_gemm_noalloc_validation(lib):
     assert call(M=0) == spin.SPIN_OK
 
 
+def test_f6_pair_validation(lib):
+    f = lib.spin_fwht_quant_f6
+
+    def q6(X=A, dt=spin.SPIN_F16, M=4, K=12288, had=12288, xf=A, xsum=A, xs=A):
+        return f(X, dt, M, K, had, xf, xsum, xs, None)
+
+    for name in ("X", "xf", "xsum", "xs"):
+        assert q6(**{name: None}) == spin.SPIN_ERR_NULL, name
+        assert q6(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert q6(dt=spin.SPIN_F32) == spin.SPIN_ERR_UNSUPPORTED
+    assert q6(had=4096) == spin.SPIN_ERR_UNSUPPORTED
+    assert q6(K=4096) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(M=0) == spin.SPIN_OK
+
+    g = lib.spin_w4a4_gemm_f6
+
+    def g6(xf=A, xsum=A, xs=A, w=A, ws_=A, M=4, N=4, K=12288, y=A, acc=None):
+        return g(xf, xsum, xs, w, ws_, M, N, K, y, acc, None)
+
+    for name in ("xf", "xsum", "xs", "w", "ws_", "y"):
+        assert g6(**{name: None}) == spin.SPIN_ERR_NULL, name
+    for name in ("xf", "xsum", "xs", "w", "ws_", "y", "acc"):
+        assert g6(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert g6(K=128) == spin.SPIN_ERR_BAD_SHAPE
+    assert g6(K=8192 + 64) == spin.SPIN_ERR_BAD_SHAPE
+    assert g6(K=65536 + 128) == spin.SPIN_ERR_BAD_SHAPE
+    assert g6(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert g6(M=0) == spin.SPIN_OK and g6(N=0) == spin.SPIN_OK
+
+
 def test_kv_qkv_validation(lib):
     f = lib.spin_kv_qkv
 
