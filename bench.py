@@ -37,13 +37,13 @@ INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA
 FP6_PEAK_TOPS = 10100.0       # MI355X dense FP6 / FP4 MFMA (the instruction the down_proj GEMM issues)
 M, K, N, HAD_N = 4096, 12288, 4096, 12288
 FWHT_BYTES_PER_TOKEN = 2 * K + K // 2 + 4          # fp16 in + packed codes + fp32 scale
-# The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2180.2
+# The VALU view of fwht_quant_k12288_mfma: one wave per row issues 2181.2
 # VALU instructions, 72 of them MFMA (rocprofv3 SQ_INSTS_VALU and
-# SQ_INSTS_MFMA over SQ_WAVES on the down_proj workload), so 2108.2 vector
+# SQ_INSTS_MFMA over SQ_WAVES on the down_proj workload), so 2109.2 vector
 # lane-operations per lane for its 192 elements (the hi/lo split, the
-# 50-operation H12, absmax, quantize and pack): 10.98 per element, against
+# 50-operation H12, absmax, quantize and pack): 10.99 per element, against
 # the chip's 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations per second.
-FWHT_VALU_OPS_PER_ELEMENT = (8930176.0 - 294912.0) / 4096.0 / 192.0
+FWHT_VALU_OPS_PER_ELEMENT = (8934272.0 - 294912.0) / 4096.0 / 192.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 KV_T, KV_H, KV_D = 4096, 32, 128
 KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp16 scale
@@ -58,13 +58,15 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "0be8bc922ec664bc", "spin_device.h": "bbe2e2331921046d"},
-                  "read": 101818183, "write": 25297008},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "a180deb96cefad8b", "w4a4_gemm_fp6.hip": "dcff8962850f1d08",
-                              "gemm_common.h": "6b6cc92bfd8335b5", "spin_device.h": "bbe2e2331921046d"},
-                 "read": 151586563, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "323482a3630af890", "spin_device.h": "bbe2e2331921046d"},
-                "read": 33636638, "write": 8650752},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "4ccb14bb05727866", "fwht12288.h": "9e0d6eff0b1cbb5b",
+                              "spin_device.h": "b68cbc5c5b3ea074"},
+                  "read": 101769289, "write": 25296987},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "0f836c55417e3db6", "w4a4_gemm_fp6.hip": "225ef16659370989",
+                              "gemm_fp6_tile.h": "64460fbf4b90bf13", "gemm_common.h": "6b6cc92bfd8335b5",
+                              "spin_device.h": "b68cbc5c5b3ea074"},
+                 "read": 151560585, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "b68cbc5c5b3ea074"},
+                "read": 33640302, "write": 8650752},
 }
 
 
