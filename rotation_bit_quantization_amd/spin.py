@@ -89,19 +89,33 @@ def spin_status_string(status: int) -> str:
     return load().spin_status_string(int(status)).decode()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream):
+    """The hipStream_t to launch on, as an integer: torch's current stream on the
+    current device unless one is given."""
     if stream is None:
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if _raw_stream is not None and _cur_device is not None:
+            return _raw_stream(_cur_device())
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _check(t, name, dtypes, shape=None):
+    """Raise unless t is a contiguous GPU tensor of one of `dtypes` (and `shape`)."""
+    try:
+        if t.is_cuda and t.dtype in dtypes and (shape is None or t.shape == shape) and t.is_contiguous():
+            return
+    except AttributeError:
+        pass
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -110,8 +124,7 @@ def _check(t, name, dtypes, shape=None):
         raise ValueError(f"{name} must be contiguous")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _raise(fn, status):
