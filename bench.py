@@ -62,9 +62,9 @@ TRAFFIC = {
                               "spin_device.h": "b68cbc5c5b3ea074"},
                   "read": 101769289, "write": 25296987},
     "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "0f836c55417e3db6", "w4a4_gemm_fp6.hip": "225ef16659370989",
-                              "gemm_fp6_tile.h": "64460fbf4b90bf13", "gemm_common.h": "6b6cc92bfd8335b5",
+                              "gemm_fp6_tile.h": "91e29af5d18bdc7e", "gemm_common.h": "6b6cc92bfd8335b5",
                               "spin_device.h": "b68cbc5c5b3ea074"},
-                 "read": 151560585, "write": 67108864},
+                 "read": 151560713, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "b68cbc5c5b3ea074"},
                 "read": 33640302, "write": 8650752},
 }
