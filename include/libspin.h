@@ -48,16 +48,22 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status and dtype travel as plain ints: every int a caller passes is a
+   valid argument (an unknown dtype is rejected with SPIN_ERR_UNSUPPORTED,
+   spin_status_string names an unknown status), which an enum type would not
+   allow in C++. */
+typedef int spin_status;
+enum {
     SPIN_OK = 0,
     SPIN_ERR_NULL = 1,          /* a required pointer is NULL                      */
     SPIN_ERR_BAD_SHAPE = 2,     /* a size is negative, not a required multiple, or too large */
     SPIN_ERR_MISALIGNED = 3,    /* a tensor pointer is not 16-byte aligned         */
     SPIN_ERR_UNSUPPORTED = 4,   /* unsupported Hadamard order, dtype or flag value */
     SPIN_ERR_HIP = 5            /* the HIP runtime reported an error               */
-} spin_status;
+};
 
-typedef enum { SPIN_F32 = 0, SPIN_F16 = 1 } spin_dtype;
+typedef int spin_dtype;
+enum { SPIN_F32 = 0, SPIN_F16 = 1 };
 
 /* Largest row length spin_fwht_quant accepts. */
 #define SPIN_FWHT_MAX_K 32768
@@ -159,8 +165,9 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
  * ((k % 64) / 32) * 768 + (r % 32) * 24 + ((k % 32) / 16) * 12 of it, in field
  * sigma(k % 16) of those 12 bytes read as a 96-bit little-endian number (field
  * p at bits 6p .. 6p + 5), sigma = 0 1 12 2 3 14 4 5 11 6 7 13 8 9 15 10.
- * Rows are rounded up to a multiple of 32 (rows past M are never read into a
- * result); K % 64 == 0.  1.5 bytes per code.
+ * Rows are rounded up to a multiple of 32; the rows past M are padding that
+ * spin_fwht_quant_f6 does not write and that no result depends on (they hold
+ * whatever the buffer held).  K % 64 == 0.  1.5 bytes per code.
  */
 #define SPIN_F6_BYTES(M, K) ((size_t)(((M) + 31) / 32) * ((size_t)(K) / 64) * 1536)
 

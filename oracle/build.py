@@ -23,6 +23,30 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(HERE, "liboracle_gemm_san.so")
+
+
+def build_sanitized() -> str:
+    """The same routine built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (no recovery) into liboracle_gemm_san.so; a process loading it preloads
+    gcc's libasan (see sanitizer_preload)."""
+    tmp = SAN_LIB + ".tmp"
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fopenmp", "-fPIC", "-shared", "-std=c11", SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def sanitizer_preload() -> str:
+    """LD_PRELOAD value for a process that loads liboracle_gemm_san.so."""
+    libs = []
+    for name in ("libasan.so", "libubsan.so"):
+        out = subprocess.run(["gcc", "-print-file-name=" + name], capture_output=True, text=True, check=True)
+        libs.append(out.stdout.strip())
+    return ":".join(libs)
+
+
 if __name__ == "__main__":
     print(build(force=True))
     sys.exit(0)

@@ -59,6 +59,43 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
+HOSTSAN_LIB = os.path.join(OBJ, "libspin_hostsan.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it also holds
+    the UndefinedBehaviorSanitizer handlers); a process loading the
+    host-sanitized library preloads it."""
+    llvm = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(llvm), reverse=True) if os.path.isdir(llvm) else []:
+        rt = os.path.join(llvm, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(rt):
+            return rt
+    raise RuntimeError("clang AddressSanitizer runtime not found")
+
+
+def build_host_sanitized() -> str:
+    """Link a second libspin, libspin_hostsan.so under _build/, whose host
+    code (abi.cpp: argument validation, dispatch, scratch and occupancy
+    caches) is built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (no recovery); the GPU code objects are the ones build() compiled.  Each
+    sanitizer flag applies to the host pass only."""
+    os.makedirs(OBJ, exist_ok=True)
+    kernels = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "abi.cpp"]
+    if not all(os.path.exists(o) for o in kernels):
+        build()
+    obj = os.path.join(OBJ, "abi_hostsan.o")
+    host_only = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"):
+        host_only += ["-Xarch_host", f]
+    cmd = [hipcc()] + _flags() + ["-O1", "-g"] + host_only + ["-c", os.path.join(CSRC, "abi.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on abi.cpp (host sanitizers):\n{r.stdout}\n{r.stderr}")
+    _link([obj] + kernels, HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source, link libspin.so and libspin_probe.so; returns the
     path of libspin.so."""

@@ -39,7 +39,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libspin.so")
+    """The in-tree libspin.so, or the build SPIN_LIBRARY names (the
+    host-sanitized one of the sanitizer tests); there is no other fallback."""
+    return os.environ.get("SPIN_LIBRARY") or os.path.join(_HERE, "libspin.so")
 
 
 class SpinError(RuntimeError):
