@@ -32,12 +32,16 @@ def _fields_of_96(words):
 
 
 def decode(buf, M, K):
-    """Bytes of the layout -> codes int8 [M, K]; also checks that every field's top two bits are zero."""
+    """Bytes of the layout -> codes int8 [M, K]; also checks that every field
+    of rows 0 .. M - 1 has its top two bits zero (the rows that pad the last
+    block of 32 are not part of the contract: nothing writes them)."""
     RB, KS = (M + 31) // 32, K // 64
     b = np.asarray(buf, np.uint8).reshape(RB, KS, 2, 32, 2, 12)
     words = b.reshape(RB, KS, 2, 32, 2, 3, 4).view("<u4").reshape(RB, KS, 2, 32, 2, 3)
     fields = _fields_of_96(words)                       # [RB, KS, half, row, g, p]
-    assert (fields >> 4 == 0).all(), "a field's top bits are set"
+    real = (np.arange(RB)[:, None] * 32 + np.arange(32)[None, :]) < M       # [RB, row]
+    assert (fields >> 4 == 0)[real[:, None, None, :, None, None].repeat(KS, 1).repeat(2, 2)
+                               .repeat(2, 4).repeat(16, 5)].all(), "a field's top bits are set"
     codes_by_j = fields[..., SIGMA] - 8                 # [RB, KS, half, row, g, j]
     c = codes_by_j.transpose(0, 3, 1, 2, 4, 5).reshape(RB * 32, K)   # row, then k = ks*64+half*32+g*16+j
     return c[:M].astype(np.int8)
