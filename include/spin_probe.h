@@ -46,6 +46,20 @@ spin_status spin_probe_mfma(int kind, int blocks, int iters, const uint32_t* ope
  * of 16, blocks out of [1, 2^20]), SPIN_ERR_MISALIGNED, SPIN_ERR_HIP. */
 spin_status spin_probe_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, void* stream);
 
+/* LDS throughput of one compute unit: `blocks` workgroups of 512 threads
+ * (eight waves, one workgroup per CU: each holds 96 KB) each fill 64 KB of LDS and then run `iters` rounds of
+ * accesses in the patterns of the FP6 GEMM's operand stages.  mode 0: each
+ * lane reads 48 bytes per round as six 8-byte loads from 24-byte rows (lane l
+ * on row l % 32 of the 768-byte region of k-half l / 32, the MFMA operand
+ * reads); mode 1: the same addresses written (the converted fields); mode 2:
+ * 48 bytes per round as three 16-byte loads from consecutive addresses.
+ * `timing`: 4 int64 per workgroup: shader-cycle counter at start and end,
+ * 100 MHz real-time counter at start and end.  `sink`: one uint32, written only
+ * if the data meets a fixed improbable value.  Errors: SPIN_ERR_NULL,
+ * SPIN_ERR_BAD_SHAPE (mode not 0, 1 or 2, blocks or iters out of [1, 2^20] /
+ * [1, 2^24]), SPIN_ERR_MISALIGNED, SPIN_ERR_HIP. */
+spin_status spin_probe_lds(int mode, int blocks, int iters, int64_t* timing, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

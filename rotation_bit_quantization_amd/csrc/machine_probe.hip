@@ -108,6 +108,71 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read(const u4v* __restric
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// LDS throughput, eight waves per workgroup (one per CU) over 64 KB, in the access
+// patterns of the FP6 GEMM's operand stages: mode 0 reads and mode 1 writes
+// 24-byte rows with three 8-byte accesses per lane (lane l on row l % 32 of
+// the 768-byte region of k-half l / 32, as the MFMA operand reads and the
+// field writes do); mode 2 reads 16 bytes per lane from consecutive
+// addresses.  Every address stays below 48 KB + 24.  timing: 4 int64 per
+// workgroup (shader cycles, 100 MHz real time, start and end, taken by
+// thread 0 after a barrier on each side).
+constexpr int kLdsThreads = 512;
+template <int MODE>
+__global__ __launch_bounds__(kLdsThreads) void probe_lds(int iters, int64_t* __restrict__ timing,
+                                                         uint32_t* __restrict__ sink) {
+    // 96 KB, of which the first 64 KB are used: more than half the CU's LDS,
+    // so that no two workgroups share a compute unit
+    __shared__ __attribute__((aligned(16))) uint8_t lds[98304];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < 65536 / 4; i += kLdsThreads) reinterpret_cast<uint32_t*>(lds)[i] = i * 2654435761u;
+    __syncthreads();
+    // modes 0, 1: base < 8 * 3072 = 24576; the step offset < 8192 and the
+    // second group +12288: below 45056 + 24.  mode 2: base < 8 * 1024, the
+    // step offset < 16384 and the group offsets < 24576: below 49152.
+    const uint32_t base = MODE == 2 ? wave * 1024 + lane * 16 : wave * 3072 + (lane >> 5) * 768 + (lane & 31) * 24;
+    uint64_t acc = 0, v = tid;
+    int64_t c0 = 0, t0 = 0;
+    if (tid == 0) {
+        c0 = clock64();
+        t0 = wall_clock64();
+    }
+    for (int it = 0; it < iters; ++it) {
+        const uint32_t o = (it & 7) * (MODE == 2 ? 2048 : 1024);
+        if (MODE == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint64_t* p = reinterpret_cast<const uint64_t*>(lds + base + o + j * 12288);
+                acc ^= p[0] ^ p[1] ^ p[2];
+            }
+        } else if (MODE == 1) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint64_t* p = reinterpret_cast<uint64_t*>(lds + base + o + j * 12288);
+                p[0] = v;
+                p[1] = v + 1;
+                p[2] = v + 2;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const u4v q = *reinterpret_cast<const u4v*>(lds + base + o + j * 8192);
+                acc ^= q[0] ^ q[1] ^ q[2] ^ q[3];
+            }
+        }
+        v += 3;
+        asm volatile("" : "+v"(acc), "+v"(v));
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t* t = timing + 4 * blockIdx.x;
+        t[0] = c0;
+        t[1] = clock64();
+        t[2] = t0;
+        t[3] = wall_clock64();
+    }
+    if ((acc ^ lds[tid * 7]) == 0x9E3779B97F4A7C15ull) sink[0] = static_cast<uint32_t>(acc);
+}
+
 }  // namespace
 
 extern "C" spin_status spin_probe_mfma(int kind, int blocks, int iters, const uint32_t* operands, int64_t* timing,
@@ -133,5 +198,21 @@ extern "C" spin_status spin_probe_read(const void* buf, size_t bytes, int blocks
     if (reinterpret_cast<uintptr_t>(buf) & 15u) return SPIN_ERR_MISALIGNED;
     hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u4v*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? SPIN_OK : SPIN_ERR_HIP;
+}
+
+extern "C" spin_status spin_probe_lds(int mode, int blocks, int iters, int64_t* timing, uint32_t* sink,
+                                      void* stream) {
+    if (!timing || !sink) return SPIN_ERR_NULL;
+    if (mode < 0 || mode > 2 || blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
+        return SPIN_ERR_BAD_SHAPE;
+    if (reinterpret_cast<uintptr_t>(timing) & 15u) return SPIN_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == 0)
+        hipLaunchKernelGGL(probe_lds<0>, dim3(blocks), dim3(kLdsThreads), 0, s, iters, timing, sink);
+    else if (mode == 1)
+        hipLaunchKernelGGL(probe_lds<1>, dim3(blocks), dim3(kLdsThreads), 0, s, iters, timing, sink);
+    else
+        hipLaunchKernelGGL(probe_lds<2>, dim3(blocks), dim3(kLdsThreads), 0, s, iters, timing, sink);
     return hipGetLastError() == hipSuccess ? SPIN_OK : SPIN_ERR_HIP;
 }

@@ -1,6 +1,7 @@
 """Machine probes through libspin_probe (include/spin_probe.h): the sustained
 dense MFMA rate of the hot path's three matrix instructions with the shader
-clock meanwhile, and the streaming read bandwidth of HBM.  bench.py reports
+clock meanwhile, the streaming read bandwidth of HBM, and the LDS throughput
+of one compute unit in the FP6 GEMM's access patterns.  bench.py reports
 them beside the published peaks; nothing in the hot path uses them.
 
 Torch only provides device memory and the stream.
@@ -16,7 +17,7 @@ from .timing import hip_events
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
-EXPORTED_SYMBOLS = ("spin_probe_mfma", "spin_probe_read")
+EXPORTED_SYMBOLS = ("spin_probe_mfma", "spin_probe_read", "spin_probe_lds")
 # v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16, v_mfma_scale_f32_32x32x64_f8f6f4 (FP6)
 OPS_PER_MFMA = {0: 2 * 32 * 32 * 32, 1: 2 * 32 * 32 * 16, 2: 2 * 32 * 32 * 64}
 
@@ -36,6 +37,7 @@ def load():
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.spin_probe_mfma.argtypes = [i, i, i, vp, vp, vp]
     lib.spin_probe_read.argtypes = [vp, ctypes.c_size_t, i, vp, vp]
+    lib.spin_probe_lds.argtypes = [i, i, i, vp, vp, vp]
     for name in EXPORTED_SYMBOLS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -123,3 +125,29 @@ def read_bandwidth(nbytes: int = 2 << 30, blocks_per_cu: int = 8) -> dict:
     del buf
     ms = float(np.median(times))
     return {"tbps": nbytes / (ms * 1e-3) / 1e12, "ms": ms, "bytes": nbytes}
+
+
+LDS_BYTES_PER_ROUND = 48          # per thread, every mode
+
+
+def lds_rate(mode: int, iters: int = 4096) -> dict:
+    """LDS bytes per shader cycle of one compute unit (one workgroup of eight
+    waves per CU, median over workgroups): mode 0 the FP6 GEMM's operand reads,
+    1 its field writes, 2 contiguous 16-byte reads."""
+    import torch
+    lib = load()
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    timing = torch.zeros(cus * 4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        rc = lib.spin_probe_lds(mode, cus, iters, timing.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"spin_probe_lds failed ({rc})")
+    torch.cuda.synchronize()
+    t = timing.cpu().numpy().reshape(-1, 4).astype(np.float64)
+    cycles = t[:, 1] - t[:, 0]
+    ghz = np.median(cycles / ((t[:, 3] - t[:, 2]) / 1e8)) / 1e9
+    per_cu = 512.0 * iters * LDS_BYTES_PER_ROUND / cycles
+    return {"bytes_per_clk_per_cu": float(np.median(per_cu)), "clock_ghz": float(ghz)}

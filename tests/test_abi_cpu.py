@@ -315,7 +315,7 @@ def test_probe_header_declares_the_binding_symbols():
 
 
 def test_probe_symbols_and_validation(probe):
-    for name in ("spin_probe_mfma", "spin_probe_read"):
+    for name in ("spin_probe_mfma", "spin_probe_read", "spin_probe_lds"):
         assert hasattr(probe, name)
     NULL, BAD, MIS = 1, 2, 3
     assert probe.spin_probe_mfma(0, 1, 1, None, A, None) == NULL
@@ -329,3 +329,10 @@ def test_probe_symbols_and_validation(probe):
     assert probe.spin_probe_read(A, 24, 1, A, None) == BAD
     assert probe.spin_probe_read(A, 16, 0, A, None) == BAD
     assert probe.spin_probe_read(U, 16, 1, A, None) == MIS
+    assert probe.spin_probe_lds(0, 1, 1, None, A, None) == NULL
+    assert probe.spin_probe_lds(0, 1, 1, A, None, None) == NULL
+    assert probe.spin_probe_lds(3, 1, 1, A, A, None) == BAD
+    assert probe.spin_probe_lds(-1, 1, 1, A, A, None) == BAD
+    assert probe.spin_probe_lds(0, 0, 1, A, A, None) == BAD
+    assert probe.spin_probe_lds(2, 1, 0, A, A, None) == BAD
+    assert probe.spin_probe_lds(1, 1, 1, U, A, None) == MIS

@@ -28,3 +28,13 @@ def test_mfma_rate_is_below_the_peak_and_the_clock_is_plausible(kind, peak):
 def test_read_bandwidth_is_below_hbm_peak():
     r = machine.read_bandwidth(nbytes=1 << 30)
     assert 1.0 < r["tbps"] < 8.2, r
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_lds_rate_is_below_the_lds_width(mode):
+    """One CU's LDS moves at most 128 bytes per cycle per direction on this
+    family (a wider port would still bound it by 256); a working probe moves
+    more than 16."""
+    r = machine.lds_rate(mode, iters=1024)
+    assert 16.0 < r["bytes_per_clk_per_cu"] < 260.0, r
+    assert 1.0 < r["clock_ghz"] < 2.5, r
