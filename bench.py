@@ -58,15 +58,15 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "4ccb14bb05727866", "fwht12288.h": "9e0d6eff0b1cbb5b",
-                              "spin_device.h": "b68cbc5c5b3ea074"},
-                  "read": 101769289, "write": 25296987},
+    "fwht_quant": {"sources": {"fwht_quant.hip": "4ccb14bb05727866", "fwht12288.h": "007b396e763ffa6e",
+                              "spin_device.h": "cf499208765bf25d"},
+                  "read": 101797973, "write": 25296968},
     "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "0f836c55417e3db6", "w4a4_gemm_fp6.hip": "225ef16659370989",
-                              "gemm_fp6_tile.h": "91e29af5d18bdc7e", "gemm_common.h": "6b6cc92bfd8335b5",
-                              "spin_device.h": "b68cbc5c5b3ea074"},
-                 "read": 151560713, "write": 67108864},
-    "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "b68cbc5c5b3ea074"},
-                "read": 33640302, "write": 8650752},
+                              "gemm_fp6_tile.h": "27e1570b43e8a48e", "gemm_common.h": "6b6cc92bfd8335b5",
+                              "spin_device.h": "cf499208765bf25d"},
+                 "read": 151554255, "write": 67108864},
+    "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "cf499208765bf25d"},
+                "read": 33640282, "write": 8650752},
 }
 
 
@@ -215,18 +215,23 @@ def machine_ceilings(fwht_tbps, gemm_tops):
     """Measured ceilings of this GPU (libspin_probe), reported beside the
     published peaks that the roofline fractions use: the INT8 and FP16 MFMA
     instructions the hot path issues, run back to back on the hot path's kind of
-    data by eight waves per CU, with the shader clock meanwhile, and a streaming
-    read of 2 GiB."""
+    data by eight waves per CU, with the shader clock meanwhile, a streaming
+    read of 2 GiB, and one CU's LDS bytes per cycle in the FP6 GEMM's access
+    patterns (operand reads, field writes) and for contiguous 16-byte reads."""
     from rotation_bit_quantization_amd import machine
     i8 = machine.mfma_rate(0)
     f16 = machine.mfma_rate(1)
     f6 = machine.mfma_rate(2)
     rd = machine.read_bandwidth()
+    lds = [machine.lds_rate(m) for m in (0, 1, 2)]
     return {
         "mfma_i32_32x32x32_i8": {"tops": round(i8["tops"], 1), "clock_ghz": round(i8["clock_ghz"], 3)},
         "mfma_f32_32x32x16_f16": {"tflops": round(f16["tops"], 1), "clock_ghz": round(f16["clock_ghz"], 3)},
         "mfma_scale_f32_32x32x64_fp6": {"tops": round(f6["tops"], 1), "clock_ghz": round(f6["clock_ghz"], 3)},
         "hbm_read_tbps": round(rd["tbps"], 3),
+        "lds_bytes_per_clk_per_cu": {"fp6_operand_reads_b64": round(lds[0]["bytes_per_clk_per_cu"], 1),
+                                     "fp6_field_writes_b64": round(lds[1]["bytes_per_clk_per_cu"], 1),
+                                     "contiguous_reads_b128": round(lds[2]["bytes_per_clk_per_cu"], 1)},
         "w4a4_gemm_frac_of_measured_int8": round(gemm_tops / i8["tops"], 4),
         "w4a4_gemm_frac_of_measured_fp6": round(gemm_tops / f6["tops"], 4),
         "fwht_quant_frac_of_measured_read": round(fwht_tbps / rd["tbps"], 4),

@@ -372,7 +372,7 @@ __device__ __forceinline__ void fwht12288_row_f6(const __half* __restrict__ X, s
         sum = __builtin_amdgcn_sdot8(static_cast<int>(w.x), 0x11111111, sum, false);
         sum = __builtin_amdgcn_sdot8(static_cast<int>(w.y), 0x11111111, sum, false);
         uint32_t o[3];
-        spread16(w.x ^ 0x88888888u, w.y ^ 0x88888888u, o);
+        spread16_offset(w.x, w.y, o);
         *reinterpret_cast<uint3*>(out + a * 16 * 1536) = make_uint3(o[0], o[1], o[2]);
     }
 #pragma unroll

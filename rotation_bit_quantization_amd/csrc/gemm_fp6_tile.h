@@ -18,8 +18,9 @@
 //
 // Conversion: a 16-byte chunk (32 codes of one row) becomes one lane's MFMA
 // operand, six dwords holding 32 consecutive 6-bit fields.  Each pair of
-// source dwords (16 nibbles, after the XOR) is spread into three dwords with
-// nine mask / shift / funnel-shift instructions; the nibble -> field order
+// source dwords (16 nibbles) is spread into three dwords with nine shift and
+// three-input bit instructions that also flip the top bit of every code
+// (spread16_offset); the nibble -> field order
 // this gives is the same for both operands, so the dot product over k is
 // unchanged.
 //
@@ -103,8 +104,8 @@ __device__ __forceinline__ void chunk_to_fp6(uint4 q, uint32_t* o, int& sum) {
     sum = __builtin_amdgcn_sdot8(static_cast<int>(q.y), 0x11111111, sum, false);
     sum = __builtin_amdgcn_sdot8(static_cast<int>(q.z), 0x11111111, sum, false);
     sum = __builtin_amdgcn_sdot8(static_cast<int>(q.w), 0x11111111, sum, false);
-    spread16(q.x ^ 0x88888888u, q.y ^ 0x88888888u, o);
-    spread16(q.z ^ 0x88888888u, q.w ^ 0x88888888u, o + 3);
+    spread16_offset(q.x, q.y, o);
+    spread16_offset(q.z, q.w, o + 3);
 }
 
 // Keeps three computed dwords where they are in the instruction stream (no
@@ -217,7 +218,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
         const uint32_t a = half ? q.z : q.x, b = half ? q.w : q.y;
         sum = __builtin_amdgcn_sdot8(static_cast<int>(a), 0x11111111, sum, false);
         sum = __builtin_amdgcn_sdot8(static_cast<int>(b), 0x11111111, sum, false);
-        spread16(a ^ 0x88888888u, b ^ 0x88888888u, o + 3 * half);
+        spread16_offset(a, b, o + 3 * half);
         pin3(o + 3 * half);
     };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
@@ -484,7 +485,7 @@ __device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, c
                     const uint32_t a = half ? q.z : q.x, b = half ? q.w : q.y;
                     sumB = __builtin_amdgcn_sdot8(static_cast<int>(a), 0x11111111, sumB, false);
                     sumB = __builtin_amdgcn_sdot8(static_cast<int>(b), 0x11111111, sumB, false);
-                    spread16(a ^ 0x88888888u, b ^ 0x88888888u, o + 3 * half);
+                    spread16_offset(a, b, o + 3 * half);
                     pin3(o + 3 * half);
                     if (half) put(lds + dst + dstB + ks * 2 * kF6Region, o);
                 }

@@ -297,16 +297,22 @@ __device__ __forceinline__ bool any_near_tie8(const uint32_t* f) {
     return min(min(m01, m23), min(m45, m67)) < 5u;
 }
 
-// FP6 operand fields.  Sixteen offset nibbles u = q + 8 (two dwords, nibble
-// k at bits 4k of a:b) -> sixteen 6-bit fields (three dwords): nibble k goes
-// to field sigma(k) (bits 6 sigma(k) .. + 5 of o[0]:o[1]:o[2]) with
-// sigma = 0 1 12 2 3 14 4 5 11 6 7 13 8 9 15 10, its four bits in the field's
-// low bits and the top two bits zero, so that the field is the FP6 E2M3
-// value u / 8.  Nine mask / shift / funnel-shift instructions.
-__device__ __forceinline__ void spread16(uint32_t a, uint32_t b, uint32_t* o) {
-    o[0] = (a & 0x0F00F00Fu) | ((a & 0x300F00F0u) << 2);
-    o[1] = (b & 0xF00F00F0u) | __builtin_amdgcn_alignbit(b & 0x00F00F00u, a, 30);
-    o[2] = (a & 0x00F00F00u) | ((b & 0x0F00F00Fu) << 2);
+// FP6 operand fields.  Sixteen two's-complement nibbles q (two dwords, nibble
+// k at bits 4k of a:b) -> sixteen 6-bit fields (three dwords) holding the
+// offset codes u = q + 8: nibble k goes to field sigma(k) (bits 6 sigma(k) ..
+// + 5 of o[0]:o[1]:o[2]) with sigma = 0 1 12 2 3 14 4 5 11 6 7 13 8 9 15 10,
+// u in the field's low four bits and the top two bits zero, so that the field
+// is the FP6 E2M3 value u / 8.  u is q with its top bit flipped; the flips
+// are not applied to the inputs but to the outputs, where they are bit 3 of
+// every field, merged into the masking: per output dword one shift (or funnel
+// shift) and two three-input bit operations, (x & M) ^ C and (y & M') ^ that,
+// nine instructions in all.
+__device__ __forceinline__ void spread16_offset(uint32_t a, uint32_t b, uint32_t* o) {
+    // bitop3 table 0x6A: (S0 & S1) ^ S2 (entry index S0 S1 S2, high to low)
+    auto and_xor = [](uint32_t x, uint32_t m, uint32_t c) { return __builtin_amdgcn_bitop3_b32(x, m, c, 0x6A); };
+    o[0] = and_xor(a << 2, 0xC03C03C0u, and_xor(a, 0x0F00F00Fu, 0x08208208u));
+    o[1] = and_xor(__builtin_amdgcn_alignbit(b, a, 30), 0x03C03C03u, and_xor(b, 0xF00F00F0u, 0x82082082u));
+    o[2] = and_xor(b << 2, 0x3C03C03Cu, and_xor(a, 0x00F00F00u, 0x20820820u));
 }
 
 }  // namespace spin
