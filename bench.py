@@ -216,19 +216,28 @@ def machine_ceilings(fwht_tbps, gemm_tops):
     published peaks that the roofline fractions use: the INT8 and FP16 MFMA
     instructions the hot path issues, run back to back on the hot path's kind of
     data by eight waves per CU, with the shader clock meanwhile, a streaming
-    read of 2 GiB, and one CU's LDS bytes per cycle in the FP6 GEMM's access
-    patterns (operand reads, field writes) and for contiguous 16-byte reads."""
+    read of 2 GiB, one CU's LDS bytes per cycle in the FP6 GEMM's access
+    patterns (operand reads, field writes) and for contiguous 16-byte reads,
+    a 1 GiB device copy, and the event-timed duration of a streaming read of
+    as many bytes as kv_quant and fwht_quant move, from buffers that rotate
+    out of the caches (the floor those kernels are timed against)."""
     from rotation_bit_quantization_amd import machine
     i8 = machine.mfma_rate(0)
     f16 = machine.mfma_rate(1)
     f6 = machine.mfma_rate(2)
     rd = machine.read_bandwidth()
     lds = [machine.lds_rate(m) for m in (0, 1, 2)]
+    cp = machine.copy_rate()
+    floors = {f"{nb / 1e6:.1f} MB ({name})": round(machine.read_floor_us(nb), 2)
+              for name, nb in (("kv_quant's bytes", KV_T * KV_H * KV_BYTES_PER_GROUP),
+                               ("fwht_quant's bytes", M * FWHT_BYTES_PER_TOKEN))}
     return {
         "mfma_i32_32x32x32_i8": {"tops": round(i8["tops"], 1), "clock_ghz": round(i8["clock_ghz"], 3)},
         "mfma_f32_32x32x16_f16": {"tflops": round(f16["tops"], 1), "clock_ghz": round(f16["clock_ghz"], 3)},
         "mfma_scale_f32_32x32x64_fp6": {"tops": round(f6["tops"], 1), "clock_ghz": round(f6["clock_ghz"], 3)},
         "hbm_read_tbps": round(rd["tbps"], 3),
+        "copy_tbps": round(cp["tbps"], 3),
+        "read_floor_us": floors,
         "lds_bytes_per_clk_per_cu": {"fp6_operand_reads_b64": round(lds[0]["bytes_per_clk_per_cu"], 1),
                                      "fp6_field_writes_b64": round(lds[1]["bytes_per_clk_per_cu"], 1),
                                      "contiguous_reads_b128": round(lds[2]["bytes_per_clk_per_cu"], 1)},
@@ -237,6 +246,33 @@ def machine_ceilings(fwht_tbps, gemm_tops):
         "fwht_quant_frac_of_measured_read": round(fwht_tbps / rd["tbps"], 4),
         "note": "measured on this GPU; the roofline objects keep the published peaks",
     }
+
+
+def vendor_int8_workload(args, dev, stream):
+    """The vendor int8 GEMM (torch._int_mm; hipBLASLt on ROCm) on the down_proj
+    shape, M = N = 4096, K = 12288, with the same INT4 values held one per byte
+    and activations rotating over the buffer sets as in the timed step: a
+    reference for the W4A4 kernel, which reads half the operand bytes but has to
+    widen or convert them.  Three outputs are checked against numpy on the host."""
+    import torch
+    rng = np.random.default_rng(7)
+    sets = max(1, args.sets)
+    a0 = rng.integers(-7, 8, size=(M, K), dtype=np.int8)
+    w = rng.integers(-7, 8, size=(N, K), dtype=np.int8)
+    A = [torch.from_numpy(a0).to(dev)]
+    A += [A[0].clone() for _ in range(1, sets)]
+    B = torch.from_numpy(w).to(dev).t()            # [K, N], column-major
+    reps = max(10, args.steps)
+    for i in range(args.warmup):
+        c = torch._int_mm(A[i % sets], B)
+    torch.cuda.synchronize()
+    got = c[0, :3].cpu().numpy().astype(np.int64)
+    ref = a0[0].astype(np.int64) @ w[:3].astype(np.int64).T
+    t = _time(lambda i: torch._int_mm(A[i % sets], B), reps, stream)
+    tops = 2.0 * M * N * K / (t * 1e-3) / 1e12
+    return {"workload": "torch._int_mm (hipBLASLt) int8 x int8 -> int32, 4096 x 4096 x 12288, codes in [-7, 7]",
+            "us": t * 1e3, "tops": tops, "frac_of_int8_peak": tops / INT8_PEAK_TOPS,
+            "checked": bool(np.array_equal(got, ref))}
 
 
 def extra_workloads(args, dev, stream):
@@ -563,6 +599,7 @@ def main():
     machine = None
     if not args.no_extra:
         extra.update(extra_workloads(args, dev, stream))
+        extra["vendor_int8_gemm"] = vendor_int8_workload(args, dev, stream)
         machine = machine_ceilings(M * FWHT_BYTES_PER_TOKEN / f_s / 1e12, gemm_tops)
 
     if not args.no_extra:

@@ -151,3 +151,56 @@ def lds_rate(mode: int, iters: int = 4096) -> dict:
     ghz = np.median(cycles / ((t[:, 3] - t[:, 2]) / 1e8)) / 1e9
     per_cu = 512.0 * iters * LDS_BYTES_PER_ROUND / cycles
     return {"bytes_per_clk_per_cu": float(np.median(per_cu)), "clock_ghz": float(ghz)}
+
+
+def read_floor_us(nbytes: int, sets: int = 4, reps: int = 12, blocks_per_cu: int = 8) -> float:
+    """Mean event-timed duration of one streaming read of `nbytes` (rounded
+    down to 16) over `sets` buffers used in turn, so that each launch reads
+    data that the previous `sets - 1` launches pushed out of the caches: the
+    floor a kernel that reads that many bytes from HBM cannot beat when timed
+    the same way."""
+    import torch
+    lib = load()
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes -= nbytes % 16
+    bufs = [torch.full((nbytes // 4,), 0x3C003C00, dtype=torch.int32, device=dev) for _ in range(sets)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    he = hip_events()
+    ev = [(he.new(), he.new()) for _ in range(reps + sets)]
+    for i, (a, b) in enumerate(ev):
+        he.record(a, stream)
+        rc = lib.spin_probe_read(bufs[i % sets].data_ptr(), nbytes, cus * blocks_per_cu, sink.data_ptr(),
+                                 stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"spin_probe_read failed ({rc})")
+        he.record(b, stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([he.ms(a, b) for a, b in ev[sets:]])) * 1e3
+    he.release()
+    del bufs
+    return us
+
+
+def copy_rate(nbytes: int = 1 << 30) -> dict:
+    """Device-to-device copy of `nbytes` (torch's copy kernel): bytes read plus
+    bytes written per second, median of four."""
+    import torch
+    dev = torch.device("cuda")
+    src = torch.full((nbytes // 4,), 7, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    he = hip_events()
+    times = []
+    for rep in range(5):
+        a, b = he.new(), he.new()
+        he.record(a, stream)
+        dst.copy_(src)
+        he.record(b, stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(he.ms(a, b))
+    he.release()
+    ms = float(np.median(times))
+    return {"tbps": 2 * nbytes / (ms * 1e-3) / 1e12, "ms": ms}
