@@ -134,6 +134,13 @@ def cpu_baseline(x_host):
     t0 = time.perf_counter()
     ogemm.gemm_int_codes(qx, wq_codes)
     t_g = time.perf_counter() - t0
+    # the qkv_proj shape, 4096 tokens x 6144 x 4096, on seeded uniform codes
+    rng4 = np.random.default_rng(8)
+    qx4 = rng4.integers(-7, 8, size=(M, 4096)).astype(np.int8)
+    qw4 = rng4.integers(-7, 8, size=(6144, 4096)).astype(np.int8)
+    t0 = time.perf_counter()
+    ogemm.gemm_int_codes(qx4, qw4)
+    t_g4 = time.perf_counter() - t0
     omp = ogemm.num_threads()
     return {
         "value": rows_f * FWHT_BYTES_PER_TOKEN / t_f / 1e9,
@@ -142,8 +149,10 @@ def cpu_baseline(x_host):
         "kind": "oracle",
         "sample": (f"the whole down_proj workload: fwht_quant on all {rows_f} tokens (dense float64 "
                    f"X.H_12288 + float32 quantizer) in {t_f:.2f} s; int64 C GEMM on {rows_g} tokens x "
-                   f"{N} x {K} in {t_g:.2f} s (seeded uniform weight codes)"),
+                   f"{N} x {K} in {t_g:.2f} s (seeded uniform weight codes); int64 C GEMM at the qkv_proj "
+                   f"shape {M} x 6144 x 4096 in {t_g4:.2f} s"),
         "gemm_tops": 2.0 * rows_g * N * K / t_g / 1e12,
+        "gemm_qkv_tops": 2.0 * M * 6144 * 4096 / t_g4 / 1e12,
         "host_cpus": cores,
         "blas_threads": blas_threads,
         "omp_threads": omp,
@@ -246,6 +255,37 @@ def machine_ceilings(fwht_tbps, gemm_tops):
         "fwht_quant_frac_of_measured_read": round(fwht_tbps / rd["tbps"], 4),
         "note": "measured on this GPU; the roofline objects keep the published peaks",
     }
+
+
+def tiny_workload(args, dev, stream):
+    """The tiny configuration, X 64 x 256 fp32 (4 outlier channels x50), W
+    256 x 256: latency of its two chains, (i) fwht_quant with H_256 + the GEMM on
+    W folded with H_256, (ii) quant-only activations X.R (R a Haar rotation
+    of order 256, applied on the host) + the GEMM on W folded with R.  74 KB of
+    data: launch-bound, reported as microseconds per call."""
+    import torch
+    from rotation_bit_quantization_amd import spin, synth
+    cfg = synth.tiny_config()
+    X = torch.from_numpy(cfg["x"]).to(dev)
+    XR = torch.from_numpy((cfg["x"].astype(np.float64) @ cfg["r"].astype(np.float64)).astype(np.float32)).to(dev)
+    W = torch.from_numpy(cfg["w"]).to(dev)
+    R = torch.from_numpy(cfg["r"].astype(np.float32)).to(dev)
+    _, Wh, wsh = spin.spin_fold_rotation(W, None, 256)
+    _, Wr, wsr = spin.spin_fold_rotation(W, R, 256)
+    Xq, xs, _ = spin.spin_fwht_quant(X, 256)
+    Xq2, xs2, _ = spin.spin_fwht_quant(XR, 1)
+    Y = torch.empty((64, 256), dtype=torch.float32, device=dev)
+    reps = max(20, args.steps)
+    for _ in range(args.warmup):
+        spin.spin_fwht_quant(X, 256, Xq=Xq, x_scale=xs)
+        spin.spin_w4a4_gemm(Xq, xs, Wh, wsh, Y=Y)
+    torch.cuda.synchronize()
+    return {"workload": "X 64x256 fp32, W 256x256: (i) H_256 fwht_quant + GEMM on the H_256 fold, "
+                        "(ii) quant-only X.R + GEMM on the Haar-R fold",
+            "fwht_quant_h256_us": _time(lambda i: spin.spin_fwht_quant(X, 256, Xq=Xq, x_scale=xs), reps, stream) * 1e3,
+            "gemm_h256_us": _time(lambda i: spin.spin_w4a4_gemm(Xq, xs, Wh, wsh, Y=Y), reps, stream) * 1e3,
+            "quant_only_us": _time(lambda i: spin.spin_fwht_quant(XR, 1, Xq=Xq2, x_scale=xs2), reps, stream) * 1e3,
+            "gemm_haar_us": _time(lambda i: spin.spin_w4a4_gemm(Xq2, xs2, Wr, wsr, Y=Y), reps, stream) * 1e3}
 
 
 def vendor_int8_workload(args, dev, stream):
@@ -600,6 +640,7 @@ def main():
     if not args.no_extra:
         extra.update(extra_workloads(args, dev, stream))
         extra["vendor_int8_gemm"] = vendor_int8_workload(args, dev, stream)
+        extra["tiny"] = tiny_workload(args, dev, stream)
         machine = machine_ceilings(M * FWHT_BYTES_PER_TOKEN / f_s / 1e12, gemm_tops)
 
     if not args.no_extra:

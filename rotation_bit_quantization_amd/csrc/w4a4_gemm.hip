@@ -14,7 +14,7 @@
 //
 // Kernels: w4a4_gemm_256 (256 x 256 tiles, the general case), w4a4_gemm_wide
 // (256 x 384 tiles where they fill the last round of workgroups better),
-// w4a4_gemm_m16 (M <= 16, weight-streaming) and w4a4_gemm_basic (K not a
+// w4a4_gemm_m16 (M <= 64, weight-streaming) and w4a4_gemm_basic (K not a
 // multiple of 128).
 #include "gemm_common.h"
 #include "spin_device.h"
@@ -412,65 +412,99 @@ __global__ __launch_bounds__(kWThreads) void w4a4_gemm_wide(
 }
 
 // ---------------------------------------------------------------------------
-// w4a4_gemm_m16: decode-sized M <= 16, where the product is bound by reading
+// w4a4_gemm_m16: decode-sized M <= 64, where the product is bound by reading
 // the weights once.  One workgroup per 16 output columns; its waves (8, or 2
 // when there are enough column groups to fill the chip) split K into ranges
-// of 128-code chunks, each wave runs two 16x16x64 int8 MFMA chains over its
-// range (lane l: row / column l % 16, 16 bytes at offset 16 (l / 16) of each
-// 64-byte chunk, the MFMA pair taking bytes 0-7 then 8-15, identically for
-// both operands), and the partial accumulators are added exactly in LDS.
-// Rows beyond M and columns beyond N read the last row / column (valid
+// of 128-code chunks.  For each of the RG groups of 16 rows a wave runs two
+// 16x16x64 int8 MFMA chains over its range (lane l: row / column l % 16, 16
+// bytes at offset 16 (l / 16) of each 64-byte chunk, the MFMA pair taking bytes
+// 0-7 then 8-15, identically for both operands); every weight chunk loaded
+// serves all RG row groups.  The partial accumulators are added exactly in
+// LDS.  Rows beyond M and columns beyond N read the last row / column (valid
 // memory) and are never stored.
-template <bool WRITE_ACC, int kDecodeWaves>
+template <bool WRITE_ACC, int kDecodeWaves, int RG>
 __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
     const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ v4i part[kDecodeWaves][64];
+    __shared__ v4i part[kDecodeWaves][RG][64];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int n0 = blockIdx.x * 16;
-    const int ra = min(lane & 15, M - 1);
     const int cb = min(n0 + (lane & 15), N - 1);
     const size_t rowBytes = static_cast<size_t>(K) / 2;
-    const uint8_t* pa = Xq + static_cast<size_t>(ra) * rowBytes + 16 * (lane >> 4);
+    const uint8_t* pa[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        pa[g] = Xq + static_cast<size_t>(min(16 * g + (lane & 15), M - 1)) * rowBytes + 16 * (lane >> 4);
     const uint8_t* pb = Wq + static_cast<size_t>(cb) * rowBytes + 16 * (lane >> 4);
     // the epilogue's scales, requested before the operands so that their
     // latency hides behind the main loads
     const int col = n0 + (lane & 15);
     const float sw = w_scale[cb];
-    float sx[4];
+    float sx[RG][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sx[r] = x_scale[min((lane >> 4) * 4 + r, M - 1)];
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sx[g][r] = x_scale[min(16 * g + (lane >> 4) * 4 + r, M - 1)];
     const int chunks = K / 128;
     const int beg = (chunks * wave) / kDecodeWaves, end = (chunks * (wave + 1)) / kDecodeWaves;
-    v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
-#pragma unroll 4
+    v4i acc0[RG], acc1[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc0[g] = acc1[g] = v4i{0, 0, 0, 0};
+#pragma unroll(RG == 1 ? 4 : 2)
     for (int it = beg; it < end; ++it) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(pa + static_cast<size_t>(it) * 64);
         const uint4 qb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(it) * 64);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.x, qa.y)),
-                                                     widen16(make_uint2(qb.x, qb.y)), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.z, qa.w)),
-                                                     widen16(make_uint2(qb.z, qb.w)), acc1, 0, 0, 0);
-    }
-    part[wave][lane] = acc0 + acc1;
-    __syncthreads();
-    if (wave != 0) return;
-    v4i sum = part[0][lane];
+        const v4i b0 = widen16(make_uint2(qb.x, qb.y)), b1 = widen16(make_uint2(qb.z, qb.w));
 #pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) sum += part[w][lane];
-    if (col >= N) return;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = (lane >> 4) * 4 + r;
-        if (row < M) {
-            const int a = sum[r] >> 8;
-            float y = static_cast<float>(a) * sx[r];
-            y = y * sw;
-            Y[static_cast<size_t>(row) * N + col] = y;
-            if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+        for (int g = 0; g < RG; ++g) {
+            const uint4 qa = *reinterpret_cast<const uint4*>(pa[g] + static_cast<size_t>(it) * 64);
+            acc0[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.x, qa.y)), b0, acc0[g], 0, 0, 0);
+            acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.z, qa.w)), b1, acc1[g], 0, 0, 0);
         }
+    }
+#pragma unroll
+    for (int g = 0; g < RG; ++g) part[wave][g][lane] = acc0[g] + acc1[g];
+    __syncthreads();
+    if (wave != 0 || col >= N) return;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        v4i sum = part[0][g][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w) sum += part[w][g][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * g + (lane >> 4) * 4 + r;
+            if (row < M) {
+                const int a = sum[r] >> 8;
+                float y = static_cast<float>(a) * sx[g][r];
+                y = y * sw;
+                Y[static_cast<size_t>(row) * N + col] = y;
+                if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+            }
+        }
+    }
+}
+
+template <int kDecodeWaves, int RG>
+void launch_m16(dim3 grid, hipStream_t s, const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                const float* w_scale, int M, int N, int K, float* Y, int32_t* acc_out) {
+    if (acc_out)
+        hipLaunchKernelGGL((w4a4_gemm_m16<true, kDecodeWaves, RG>), grid, dim3(64 * kDecodeWaves), 0, s, Xq, x_scale,
+                           Wq, w_scale, M, N, K, Y, acc_out);
+    else
+        hipLaunchKernelGGL((w4a4_gemm_m16<false, kDecodeWaves, RG>), grid, dim3(64 * kDecodeWaves), 0, s, Xq,
+                           x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+}
+
+template <int kDecodeWaves>
+void launch_m16_rows(dim3 grid, hipStream_t s, const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                     const float* w_scale, int M, int N, int K, float* Y, int32_t* acc_out) {
+    switch ((M + 15) / 16) {
+        case 1: launch_m16<kDecodeWaves, 1>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        case 2: launch_m16<kDecodeWaves, 2>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        case 3: launch_m16<kDecodeWaves, 3>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        default: launch_m16<kDecodeWaves, 4>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
     }
 }
 
@@ -481,27 +515,16 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
                             int32_t* acc_out, int kernel, hipStream_t s) {
     if (kernel == 2 || (kernel == 0 && w4a4_gemm_fp6_applies(M, N, K)))
         return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
-    if (M <= 16 && K % 128 == 0) {
+    if (M <= 64 && K % 128 == 0) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         // many column groups (gate/up): two waves each, so that every wave
         // streams a longer K range; few (qkv, o_proj, down): eight waves
         const int cus = device_cu_count();
         const bool wide = cus > 0 && static_cast<long long>(grid.x) >= 4LL * cus;
-        if (wide) {
-            if (acc_out)
-                hipLaunchKernelGGL((w4a4_gemm_m16<true, 2>), grid, dim3(128), 0, s, Xq, x_scale, Wq, w_scale, M, N,
-                                   K, Y, acc_out);
-            else
-                hipLaunchKernelGGL((w4a4_gemm_m16<false, 2>), grid, dim3(128), 0, s, Xq, x_scale, Wq, w_scale, M,
-                                   N, K, Y, acc_out);
-        } else {
-            if (acc_out)
-                hipLaunchKernelGGL((w4a4_gemm_m16<true, 8>), grid, dim3(512), 0, s, Xq, x_scale, Wq, w_scale, M, N,
-                                   K, Y, acc_out);
-            else
-                hipLaunchKernelGGL((w4a4_gemm_m16<false, 8>), grid, dim3(512), 0, s, Xq, x_scale, Wq, w_scale, M,
-                                   N, K, Y, acc_out);
-        }
+        if (wide)
+            launch_m16_rows<2>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+        else
+            launch_m16_rows<8>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
         return hipGetLastError();
     }
     if (K % kStepCodes == 0) {

@@ -310,6 +310,23 @@ def test_gemm_decode_sizes(M, N, K):
     check_gemm(qx, qw, sx, sw)
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 37, 128), (32, 300, 1280), (33, 4096 + 16, 4096), (48, 6144, 4096),
+                                   (64, 256, 256), (64, 4096, 12288), (61, 24576, 4096), (64, 100, 384)])
+def test_gemm_up_to_64_rows(M, N, K):
+    """17 to 64 rows run the weight-streaming kernel with up to four 16-row
+    groups sharing each weight load: all rows, against the int64 oracle, with
+    the -8 / +7 extremes in the first rows."""
+    rng = np.random.default_rng(M * 11 + N + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    qx[0] = -8
+    qx[M - 1] = 7
+    qw[0] = -8
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw)
+
+
 @pytest.mark.parametrize("K", [128, 256, 384, 4096])
 def test_gemm_qkv_shape_wide_tiles(K):
     """M = 4096, N = 6144 (qkv_proj) runs 256 x 384 tiles: one step (shorter
