@@ -14,7 +14,7 @@
 //
 // Kernels: w4a4_gemm_256 (256 x 256 tiles, the general case), w4a4_gemm_wide
 // (256 x 384 tiles where they fill the last round of workgroups better),
-// w4a4_gemm_m16 (M <= 64, weight-streaming) and w4a4_gemm_basic (K not a
+// w4a4_gemm_m16 (M <= 128, weight-streaming) and w4a4_gemm_basic (K not a
 // multiple of 128).
 #include "gemm_common.h"
 #include "spin_device.h"
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kWThreads) void w4a4_gemm_wide(
 }
 
 // ---------------------------------------------------------------------------
-// w4a4_gemm_m16: decode-sized M <= 64, where the product is bound by reading
+// w4a4_gemm_m16: M <= 128 (decode, short prompts), where the product is bound by reading
 // the weights once.  One workgroup per 16 output columns; its waves (8, or 2
 // when there are enough column groups to fill the chip) split K into ranges
 // of 128-code chunks.  For each of the RG groups of 16 rows a wave runs two
@@ -504,7 +504,10 @@ void launch_m16_rows(dim3 grid, hipStream_t s, const uint8_t* Xq, const float* x
         case 1: launch_m16<kDecodeWaves, 1>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
         case 2: launch_m16<kDecodeWaves, 2>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
         case 3: launch_m16<kDecodeWaves, 3>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
-        default: launch_m16<kDecodeWaves, 4>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        case 4: launch_m16<kDecodeWaves, 4>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        case 5:
+        case 6: launch_m16<kDecodeWaves, 6>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
+        default: launch_m16<kDecodeWaves, 8>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out); break;
     }
 }
 
@@ -515,17 +518,21 @@ hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8
                             int32_t* acc_out, int kernel, hipStream_t s) {
     if (kernel == 2 || (kernel == 0 && w4a4_gemm_fp6_applies(M, N, K)))
         return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
-    if (M <= 64 && K % 128 == 0) {
+    if (M <= 128 && K % 128 == 0) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         // many column groups (gate/up): two waves each, so that every wave
-        // streams a longer K range; few (qkv, o_proj, down): eight waves
+        // streams a longer K range; few (qkv, o_proj, down): eight waves.
+        // Past 64 rows a wide grid leaves this kernel compute- and L2-bound
+        // (128 x 24576 x 4096: 73 us against 64 on the FP6 tiles): tiles then.
         const int cus = device_cu_count();
         const bool wide = cus > 0 && static_cast<long long>(grid.x) >= 4LL * cus;
-        if (wide)
-            launch_m16_rows<2>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
-        else
-            launch_m16_rows<8>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
-        return hipGetLastError();
+        if (M <= 64 || !wide) {
+            if (wide)
+                launch_m16_rows<2>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+            else
+                launch_m16_rows<8>(grid, s, Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out);
+            return hipGetLastError();
+        }
     }
     if (K % kStepCodes == 0) {
         const long long tiles = static_cast<long long>((N + kT - 1) / kT) * ((M + kT - 1) / kT);

@@ -46,11 +46,13 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6a(
 // The FP6 kernel wins on long reductions whose 256 x 256 tiles fill one or
 // two rounds of the compute units; with fewer tiles the int8 kernels' shorter
 // per-tile latency wins, with many rounds their higher sustained rate.
-// Up to 64 rows the weight-streaming decode kernel takes the product.
+// Up to 64 rows, and up to 128 when N / 16 < 4 CUs, the weight-streaming
+// decode kernel takes the product.
 bool w4a4_gemm_fp6_applies(int M, int N, int K) {
     if (M <= 64 || K % kF6StepCodes != 0 || K < 8192 || K > kGemmFp6MaxK) return false;
     const int cus = device_cu_count();
     if (cus <= 0) return false;
+    if (M <= 128 && (N + 15) / 16 < 4 * cus) return false;   // the weight-streaming kernel's range
     const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
     return 4 * tiles >= 3LL * cus && tiles <= 2LL * cus;
 }

@@ -311,11 +311,12 @@ def test_gemm_decode_sizes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 37, 128), (32, 300, 1280), (33, 4096 + 16, 4096), (48, 6144, 4096),
-                                   (64, 256, 256), (64, 4096, 12288), (61, 24576, 4096), (64, 100, 384)])
-def test_gemm_up_to_64_rows(M, N, K):
-    """17 to 64 rows run the weight-streaming kernel with up to four 16-row
+                                   (64, 256, 256), (64, 4096, 12288), (61, 24576, 4096), (64, 100, 384),
+                                   (65, 333, 512), (96, 4096, 4096), (100, 1000, 12288), (128, 4096, 12288)])
+def test_gemm_up_to_128_rows(M, N, K):
+    """17 to 128 rows run the weight-streaming kernel with up to eight 16-row
     groups sharing each weight load: all rows, against the int64 oracle, with
-    the -8 / +7 extremes in the first rows."""
+    the -8 / +7 extremes in the first and last rows."""
     rng = np.random.default_rng(M * 11 + N + K)
     qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
