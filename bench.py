@@ -60,13 +60,13 @@ CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
     "fwht_quant": {"sources": {"fwht_quant.hip": "4ccb14bb05727866", "fwht12288.h": "007b396e763ffa6e",
                               "spin_device.h": "cf499208765bf25d"},
-                  "read": 101797973, "write": 25296968},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "0f836c55417e3db6", "w4a4_gemm_fp6.hip": "225ef16659370989",
+                  "read": 101767006, "write": 25296931},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "57dedbf40f01d9d9", "w4a4_gemm_fp6.hip": "75eeebcdaca5d78e",
                               "gemm_fp6_tile.h": "27e1570b43e8a48e", "gemm_common.h": "6b6cc92bfd8335b5",
                               "spin_device.h": "cf499208765bf25d"},
-                 "read": 151554255, "write": 67108864},
+                 "read": 151554598, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "cf499208765bf25d"},
-                "read": 33640282, "write": 8650752},
+                "read": 33640358, "write": 8650752},
 }
 
 
