@@ -328,6 +328,23 @@ def test_gemm_up_to_128_rows(M, N, K):
     check_gemm(qx, qw, sx, sw)
 
 
+@pytest.mark.parametrize("M", [16, 17, 64, 65, 128, 129])
+@pytest.mark.parametrize("N", [16368, 16400])
+def test_gemm_dispatch_boundaries(M, N):
+    """Either side of every kernel-choice boundary: 16 / 17 and 64 / 65 rows
+    (row groups of the weight-streaming kernel), 128 / 129 rows (its end), and
+    a column grid just below and just above 4 x 256 workgroups of 16 columns
+    (two waves per workgroup instead of eight; past 64 rows, the tiles).  All
+    rows against the int64 oracle."""
+    K = 1024
+    rng = np.random.default_rng(M * 3 + N)
+    qx = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm(qx, qw, sx, sw)
+
+
 @pytest.mark.parametrize("K", [128, 256, 384, 4096])
 def test_gemm_qkv_shape_wide_tiles(K):
     """M = 4096, N = 6144 (qkv_proj) runs 256 x 384 tiles: one step (shorter
