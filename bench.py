@@ -58,15 +58,15 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # any change to that code it reports null.
 CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
-    "fwht_quant": {"sources": {"fwht_quant.hip": "4ccb14bb05727866", "fwht12288.h": "007b396e763ffa6e",
+    "fwht_quant": {"sources": {"fwht_quant.hip": "534a39ba359043de", "fwht12288.h": "aeebefa0ba05bd5b",
                               "spin_device.h": "cf499208765bf25d"},
-                  "read": 101767006, "write": 25296931},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "57dedbf40f01d9d9", "w4a4_gemm_fp6.hip": "75eeebcdaca5d78e",
+                  "read": 101756505, "write": 25296939},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "439aa19fd14b45f2", "w4a4_gemm_fp6.hip": "75eeebcdaca5d78e",
                               "gemm_fp6_tile.h": "27e1570b43e8a48e", "gemm_common.h": "6b6cc92bfd8335b5",
                               "spin_device.h": "cf499208765bf25d"},
-                 "read": 151554598, "write": 67108864},
+                 "read": 151551689, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "cf499208765bf25d"},
-                "read": 33640358, "write": 8650752},
+                "read": 33639847, "write": 8650752},
 }
 
 

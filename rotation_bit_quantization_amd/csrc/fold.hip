@@ -26,7 +26,7 @@ __device__ __forceinline__ float block_entry(const float* R, int r, int j, int i
 
 // r % 64 == 0: a 64 x 64 output tile lies inside one diagonal block.
 template <bool HAD>
-__global__ __launch_bounds__(256) void fold_gemm_tiled(const float* __restrict__ W, int K, int N,
+__global__ __launch_bounds__(256) void fold_gemm_tiled(const float* __restrict__ W, int /* K */, int N,
                                                        const float* __restrict__ R, int r,
                                                        int log2p, int has12, float norm,
                                                        float* __restrict__ W_rot) {

@@ -235,7 +235,8 @@ __device__ __forceinline__ uint2 quant16_nibbles(const f16v& u, float cr, float 
         for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuantMagic));
         w0 = pack8_magic(f);
         w1 = pack8_magic(f + 8);
-        exact = any_near_tie(f) | any_near_tie(f + 8);   // no short circuit: one branch
+        // no short circuit: one branch
+        exact = (static_cast<int>(any_near_tie(f)) | static_cast<int>(any_near_tie(f + 8))) != 0;
     }
     if (exact) {
         int c[16];
@@ -262,7 +263,7 @@ __device__ __forceinline__ void quant16_store(uint8_t* p, const f16v& u, float c
 #pragma unroll
             for (int k = 0; k < 16; ++k) f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, kQuant8Magic));
             w = make_uint4(pack4_magic8(f), pack4_magic8(f + 4), pack4_magic8(f + 8), pack4_magic8(f + 12));
-            exact = any_near_tie8(f) | any_near_tie8(f + 8);
+            exact = (static_cast<int>(any_near_tie8(f)) | static_cast<int>(any_near_tie8(f + 8))) != 0;
         }
         if (exact) {
             int c[16];

@@ -144,10 +144,12 @@ __device__ __forceinline__ void quant4_store(uint8_t* p, const float (&u)[4], fl
             f[k] = __float_as_uint(__builtin_fmaf(u[k], cr, BITS == 4 ? kQuantMagic : kQuant8Magic));
         if (BITS == 4) {
             w = ((f[0] >> 16) & 0xFu) | ((f[1] >> 12) & 0xF0u) | ((f[2] >> 8) & 0xF00u) | ((f[3] >> 4) & 0xF000u);
-            exact = near_tie(f[0]) | near_tie(f[1]) | near_tie(f[2]) | near_tie(f[3]);
+            exact = (static_cast<int>(near_tie(f[0])) | static_cast<int>(near_tie(f[1])) |
+                     static_cast<int>(near_tie(f[2])) | static_cast<int>(near_tie(f[3]))) != 0;
         } else {
             w = pack4_magic8(f);
-            exact = near_tie8(f[0]) | near_tie8(f[1]) | near_tie8(f[2]) | near_tie8(f[3]);
+            exact = (static_cast<int>(near_tie8(f[0])) | static_cast<int>(near_tie8(f[1])) |
+                     static_cast<int>(near_tie8(f[2])) | static_cast<int>(near_tie8(f[3]))) != 0;
         }
     }
     if (exact) {

@@ -140,7 +140,6 @@ constexpr int kStepBytes = kStepCodes / 2;
 constexpr int kStageBytes = 2 * kT * kStepBytes;   // A then B
 constexpr int kStages = 4;
 constexpr int kGemmThreads = 1024;
-constexpr int kGemmMinK = kStepCodes;
 
 template <bool WRITE_ACC>
 __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
@@ -452,16 +451,38 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void w4a4_gemm_m16(
     v4i acc0[RG], acc1[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) acc0[g] = acc1[g] = v4i{0, 0, 0, 0};
-#pragma unroll(RG == 1 ? 4 : 2)
-    for (int it = beg; it < end; ++it) {
-        const uint4 qb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(it) * 64);
+    // Chunks in groups of U with every load of a group issued before its
+    // MFMAs (written out: the matrix builtins are convergent, so the compiler
+    // does not unroll a loop with a run-time trip count around them), then
+    // the remainder one at a time; beg and end are uniform across the wave.
+    constexpr int U = RG == 1 ? 4 : RG <= 2 ? 2 : 1;
+    auto step = [&](const uint4& qb, const uint4* qa) {
         const v4i b0 = widen16(make_uint2(qb.x, qb.y)), b1 = widen16(make_uint2(qb.z, qb.w));
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-            const uint4 qa = *reinterpret_cast<const uint4*>(pa[g] + static_cast<size_t>(it) * 64);
-            acc0[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.x, qa.y)), b0, acc0[g], 0, 0, 0);
-            acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa.z, qa.w)), b1, acc1[g], 0, 0, 0);
+            acc0[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa[g].x, qa[g].y)), b0, acc0[g], 0, 0, 0);
+            acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen16(make_uint2(qa[g].z, qa[g].w)), b1, acc1[g], 0, 0, 0);
         }
+    };
+    int it = beg;
+    for (; it + U <= end; it += U) {
+        uint4 qb[U], qa[U][RG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            qb[u] = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(it + u) * 64);
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                qa[u][g] = *reinterpret_cast<const uint4*>(pa[g] + static_cast<size_t>(it + u) * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(qb[u], qa[u]);
+    }
+    for (; it < end; ++it) {
+        uint4 qa[RG];
+        const uint4 qb = *reinterpret_cast<const uint4*>(pb + static_cast<size_t>(it) * 64);
+#pragma unroll
+        for (int g = 0; g < RG; ++g) qa[g] = *reinterpret_cast<const uint4*>(pa[g] + static_cast<size_t>(it) * 64);
+        step(qb, qa);
     }
 #pragma unroll
     for (int g = 0; g < RG; ++g) part[wave][g][lane] = acc0[g] + acc1[g];
