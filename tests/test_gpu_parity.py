@@ -591,7 +591,8 @@ def test_rotation_probe_matches_oracle():
 def test_r2_experiment_errors_match_oracle():
     """The errors the R2 experiment measures through libspin (random
     Hadamards and the learned rotation, block 128) equal the oracle's W4A4
-    layer error for the same float32 rotations within 1%."""
+    layer error for the same float32 rotations within 1%, and the learned
+    rotation's layer matches the oracle elementwise."""
     from rotation_bit_quantization_amd import cayley
     cfg = synth.r2_config(T=128, heads=8, head_dim=128, N=256, draws=3)
     res = cayley.r2_experiment(cfg, iters=8)
@@ -609,6 +610,19 @@ def test_r2_experiment_errors_match_oracle():
     assert abs(res["random_hadamard"]["min"] - min(draws)) <= 1e-2 * min(draws)
     assert abs(res["learned"] - err(res["R2"])) <= 1e-2 * res["learned"]
     assert res["orthogonality_error"] < 1e-12
+    # elementwise, the learned R2: the device fold + GEMM against the oracle's
+    # (codes bit-exact up to near-tie flips, Y within the end-to-end tolerance)
+    R = np.ascontiguousarray(res["R2"], dtype=np.float32)
+    _, xq_o, xs_o = oracle.fold_rotation(np.ascontiguousarray(x.T), R, 128)
+    _, wq_o, ws_o = oracle.fold_rotation(w, R, 128)
+    y_o, _ = oracle.w4a4_gemm(xq_o, xs_o, wq_o, ws_o)
+    r_dev = _dev(R)
+    _, xq, xs = spin.spin_fold_rotation(_dev(np.ascontiguousarray(x.T)), r_dev, 128)
+    _, wq, ws = spin.spin_fold_rotation(_dev(w), r_dev, 128)
+    y, _ = spin.spin_w4a4_gemm(xq, xs, wq, ws)
+    fr = code_flips(_host(xq), xq_o, axis=1)
+    fc = code_flips(_host(wq), wq_o, axis=1)
+    assert_y_close(_host(y), y_o, flip_rows=fr, flip_cols=fc)
 
 
 def test_orthogonality_check_matches_oracle():
