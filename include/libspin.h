@@ -136,6 +136,7 @@ spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_
 #define SPIN_GEMM_AUTO 0   /* the choice spin_w4a4_gemm makes */
 #define SPIN_GEMM_INT8 1   /* codes widened to int8, int8 matrix cores, int32 accumulation */
 #define SPIN_GEMM_FP6 2    /* codes as FP6 E2M3 (u = q + 8, exact), FP6 matrix cores */
+#define SPIN_GEMM_FP6_SPLITK 3   /* the FP6 tiles with K split into slices; see below */
 /* K range of the FP6 kernel: its float32 accumulator of products u_a * u_b <= 225
    is exact while 225 K < 2^24 (K < 74566; the bound stops at the power of two
    below), and its pipeline needs two steps of 128 codes. */
@@ -146,10 +147,19 @@ spin_status spin_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_
  * spin_w4a4_gemm_ex — spin_w4a4_gemm with the kernel family named: the same
  * arguments, outputs and guarantees (every family gives the same bits), for
  * callers that tune the choice for their shapes.  `kernel` is SPIN_GEMM_AUTO,
- * SPIN_GEMM_INT8 or SPIN_GEMM_FP6.
+ * SPIN_GEMM_INT8, SPIN_GEMM_FP6 or SPIN_GEMM_FP6_SPLITK.
+ * SPIN_GEMM_FP6_SPLITK (taken by AUTO for 129 or more rows whose 256 x 256
+ * tiles leave half the compute units idle, when it predicts a gain) is three
+ * launches on `stream`: Y is zeroed, the FP6 tiles of every K slice add their
+ * exact int32 partial products into Y read as int32 (atomically), and a last
+ * pass turns Y into the dequantized float32 outputs in place (and writes
+ * acc_out).  The slice count is chosen from the shape (1 when slicing does not
+ * pay).  The integer sum is exact and the epilogue the same, so the bits equal
+ * the other families'; between the launches Y holds integers.
  * Errors: SPIN_ERR_UNSUPPORTED for another `kernel` value; with
- * SPIN_GEMM_FP6, SPIN_ERR_BAD_SHAPE unless K % 128 == 0 and
- * SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K; otherwise as spin_w4a4_gemm.
+ * SPIN_GEMM_FP6 or SPIN_GEMM_FP6_SPLITK, SPIN_ERR_BAD_SHAPE unless K % 128 == 0
+ * and SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K; otherwise as
+ * spin_w4a4_gemm.
  */
 spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                               const float* w_scale, int M, int N, int K, float* Y,

@@ -142,10 +142,12 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
                               const float* w_scale, int M, int N, int K, float* Y,
                               int32_t* acc_out, int kernel, void* stream) {
     if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SPIN_ERR_NULL;
-    if (kernel != SPIN_GEMM_AUTO && kernel != SPIN_GEMM_INT8 && kernel != SPIN_GEMM_FP6)
+    if (kernel != SPIN_GEMM_AUTO && kernel != SPIN_GEMM_INT8 && kernel != SPIN_GEMM_FP6 &&
+        kernel != SPIN_GEMM_FP6_SPLITK)
         return SPIN_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > SPIN_GEMM_MAX_K) return SPIN_ERR_BAD_SHAPE;
-    if (kernel == SPIN_GEMM_FP6 && (K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_GEMM_FP6_MAX_K))
+    if ((kernel == SPIN_GEMM_FP6 || kernel == SPIN_GEMM_FP6_SPLITK) &&
+        (K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_GEMM_FP6_MAX_K))
         return SPIN_ERR_BAD_SHAPE;
     const long long tiles = (static_cast<long long>(M) + 127) / 128 * ((static_cast<long long>(N) + 127) / 128);
     if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;

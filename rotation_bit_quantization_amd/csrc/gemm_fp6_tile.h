@@ -123,17 +123,23 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 // on `lds` (three stages of kF6StageBytes, 1024-byte aligned).  Every thread of
 // the workgroup calls it; it returns once the tile's stores are issued, with
 // the first stage still holding the tile's code sums (read by the epilogue).
-template <bool WRITE_ACC>
+// By default the whole reduction; with nsteps >= 0 only the 128-code steps
+// s0 .. s0 + nsteps - 1 (at least two).  SPLIT: the exact int32 dot products of
+// that range (their own code-sum corrections applied) are added atomically
+// into Y read as int32, for a later dequantizing pass; x_scale, w_scale and
+// acc_out are not used.
+template <bool WRITE_ACC, bool SPLIT = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const float* __restrict__ x_scale,
                                           const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale,
                                           int M, int N, int K, float* __restrict__ Y,
-                                          int32_t* __restrict__ acc_out, int tm, int tn, uint8_t* lds) {
+                                          int32_t* __restrict__ acc_out, int tm, int tn, uint8_t* lds,
+                                          int s0 = 0, int nsteps = -1) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int m0 = tm * kF6T, n0 = tn * kF6T;
     const size_t rowBytes = static_cast<size_t>(K) / 2;
-    const int steps = K / kF6StepCodes;
+    const int steps = nsteps >= 0 ? nsteps : K / kF6StepCodes;
 
     // Thread (w, l) converts k-half h = l / 32 of both k-steps of row
     // 32 w + l % 32 of A and of B in every step: four 16-byte chunks, loaded
@@ -145,8 +151,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     const int h = lane >> 5;
     const uint32_t offA = static_cast<uint32_t>(min(r, M - m0 - 1)) * static_cast<uint32_t>(rowBytes) + 16u * h;
     const uint32_t offB = static_cast<uint32_t>(min(r, N - n0 - 1)) * static_cast<uint32_t>(rowBytes) + 16u * h;
-    const uint8_t* baseA = Xq + static_cast<size_t>(m0) * rowBytes;
-    const uint8_t* baseB = Wq + static_cast<size_t>(n0) * rowBytes;
+    const uint8_t* baseA = Xq + static_cast<size_t>(m0) * rowBytes + static_cast<size_t>(s0) * kF6StepBytes;
+    const uint8_t* baseB = Wq + static_cast<size_t>(n0) * rowBytes + static_cast<size_t>(s0) * kF6StepBytes;
     const uint32_t dstA = (wave * 2 + h) * kF6Region + (lane & 31) * 24;
     const uint32_t dstB = dstA + 8 * 2 * kF6Region;
     int sumA = 0, sumB = 0;
@@ -325,7 +331,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
     // epilogue: acc = sum u_a u_b -> exact dot product of the codes, then
     // Y = fl32(fl32(acc * s_x) * s_w).  Result register r of lane l holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 tile.
-    const int k64 = 64 * K;
+    const int k64 = 64 * steps * kF6StepCodes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -333,7 +339,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
             const int rt = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int row = m0 + rt;
             if (row >= M) continue;
-            const float sx = x_scale[row];
+            const float sx = SPLIT ? 0.0f : x_scale[row];
             const int sa = sums[rt];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -341,10 +347,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
                 const int col = n0 + ct;
                 if (col < N) {
                     const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa + sums[kF6T + ct]) - k64;
-                    float y = static_cast<float>(a) * sx;
-                    y = y * w_scale[col];
-                    Y[static_cast<size_t>(row) * N + col] = y;
-                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+                    if (SPLIT) {
+                        atomicAdd(reinterpret_cast<int*>(Y) + static_cast<size_t>(row) * N + col, a);
+                    } else {
+                        float y = static_cast<float>(a) * sx;
+                        y = y * w_scale[col];
+                        Y[static_cast<size_t>(row) * N + col] = y;
+                        if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+                    }
                 }
             }
         }

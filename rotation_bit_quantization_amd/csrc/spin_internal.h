@@ -36,6 +36,10 @@ hipError_t launch_kv_qkv(const void* Q, const void* K, const void* V, bool x_f16
 // The FP6 matrix-core path of launch_w4a4_gemm (exact for K <= kGemmFp6MaxK).
 constexpr int kGemmFp6MaxK = 65536;
 bool w4a4_gemm_fp6_applies(int M, int N, int K);
+int w4a4_gemm_fp6_split_slices(int M, int N, int K, bool forced);
+hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
+                                      const float* w_scale, int M, int N, int K, int slices, float* Y,
+                                      int32_t* acc_out, hipStream_t s);
 hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                                 const float* w_scale, int M, int N, int K, float* Y,
                                 int32_t* acc_out, hipStream_t s);

@@ -537,6 +537,12 @@ void launch_m16_rows(dim3 grid, hipStream_t s, const uint8_t* Xq, const float* x
 hipError_t launch_w4a4_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                             const float* w_scale, int M, int N, int K, float* Y,
                             int32_t* acc_out, int kernel, hipStream_t s) {
+    if (kernel == 3 || kernel == 0) {
+        const int slices = w4a4_gemm_fp6_split_slices(M, N, K, kernel == 3);
+        if (slices >= 2 || (kernel == 3 && slices == 1))
+            return launch_w4a4_gemm_fp6_split(Xq, x_scale, Wq, w_scale, M, N, K, slices, Y, acc_out, s);
+        if (kernel == 3) return hipErrorInvalidDevice;
+    }
     if (kernel == 2 || (kernel == 0 && w4a4_gemm_fp6_applies(M, N, K)))
         return launch_w4a4_gemm_fp6(Xq, x_scale, Wq, w_scale, M, N, K, Y, acc_out, s);
     if (M <= 128 && K % 128 == 0) {

@@ -19,13 +19,13 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
            "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6", "spin_w4a4_gemm_f6",
-           "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6",
+           "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6", "SPIN_GEMM_FP6_SPLITK",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
     SPIN_ERR_HIP = range(6)
 SPIN_F32, SPIN_F16 = 0, 1
-SPIN_GEMM_AUTO, SPIN_GEMM_INT8, SPIN_GEMM_FP6 = 0, 1, 2
+SPIN_GEMM_AUTO, SPIN_GEMM_INT8, SPIN_GEMM_FP6, SPIN_GEMM_FP6_SPLITK = 0, 1, 2, 3
 SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
@@ -180,7 +180,7 @@ def spin_w4a4_gemm(Xq, x_scale, Wq, w_scale, Y=None, acc_out=None, want_acc=Fals
                    stream=None):
     """Packed Xq [M, K/2], Wq [N, K/2] + scales -> (Y [M, N] fp32, acc [M, N] int32 or None).
 
-    ``kernel`` (SPIN_GEMM_INT8 / SPIN_GEMM_FP6) names the kernel family through
+    ``kernel`` (SPIN_GEMM_INT8 / SPIN_GEMM_FP6 / SPIN_GEMM_FP6_SPLITK) names the kernel family through
     spin_w4a4_gemm_ex; None leaves the choice to the library."""
     _check(Xq, "Xq", (torch.uint8,))
     _check(Wq, "Wq", (torch.uint8,))

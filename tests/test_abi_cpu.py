@@ -167,11 +167,13 @@ def test_gemm_ex_validation(lib):
     def call(M=4, N=4, K=8192, kernel=spin.SPIN_GEMM_FP6, y=A):
         return f(A, A, A, A, M, N, K, y, None, kernel, None)
 
-    assert call(kernel=3) == spin.SPIN_ERR_UNSUPPORTED
+    assert call(kernel=4) == spin.SPIN_ERR_UNSUPPORTED
     assert call(kernel=-1) == spin.SPIN_ERR_UNSUPPORTED
-    assert call(K=128) == spin.SPIN_ERR_BAD_SHAPE                 # below the FP6 pipeline's two steps
-    assert call(K=8192 + 64) == spin.SPIN_ERR_BAD_SHAPE           # not a multiple of 128
-    assert call(K=65536 + 128) == spin.SPIN_ERR_BAD_SHAPE         # beyond exact float32 accumulation
+    for k in (spin.SPIN_GEMM_FP6, spin.SPIN_GEMM_FP6_SPLITK):
+        assert call(K=128, kernel=k) == spin.SPIN_ERR_BAD_SHAPE         # below the FP6 pipeline's two steps
+        assert call(K=8192 + 64, kernel=k) == spin.SPIN_ERR_BAD_SHAPE   # not a multiple of 128
+        assert call(K=65536 + 128, kernel=k) == spin.SPIN_ERR_BAD_SHAPE # beyond exact float32 accumulation
+        assert call(K=256, M=0, kernel=k) == spin.SPIN_OK
     assert call(K=65536 + 128, kernel=spin.SPIN_GEMM_INT8, y=None) == spin.SPIN_ERR_NULL
     assert call(K=65536 + 128, kernel=spin.SPIN_GEMM_INT8, M=0) == spin.SPIN_OK
     assert call(K=256, M=0) == spin.SPIN_OK
