@@ -52,30 +52,64 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_split(
                            s1 - s0);
 }
 
-// Zeroes the int32 partial sums (a kernel rather than a memset, so that the
-// three launches of a split product can be captured in a graph).
-__global__ __launch_bounds__(256) void zero_partials(int32_t* __restrict__ p, size_t n) {
+// Zeroes n words of the 16-byte-aligned p (a kernel rather than a memset, so
+// that the three launches of a split product can be captured in a graph).
+__global__ __launch_bounds__(256) void zero_partials(uint32_t* __restrict__ p, size_t n) {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+    const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    uint4* q = reinterpret_cast<uint4*>(p);
+    for (size_t i = i0; i < n / 4; i += stride) q[i] = make_uint4(0, 0, 0, 0);
+    if (i0 < n % 4) p[n / 4 * 4 + i0] = 0;
 }
 
 // Row blockIdx.x of the summed int32 accumulators in Y -> the dequantized
-// float32 outputs, in place, with the epilogue arithmetic of the tile.
-template <bool WRITE_ACC>
+// float32 outputs, in place, with the epilogue arithmetic of the tile; VEC4:
+// four columns per thread (N % 4 == 0, every row 16-byte aligned).
+template <bool WRITE_ACC, bool VEC4>
 __global__ __launch_bounds__(256) void split_dequant(float* __restrict__ Y, const float* __restrict__ x_scale,
                                                      const float* __restrict__ w_scale, int N,
                                                      int32_t* __restrict__ acc_out) {
     const int row = static_cast<int>(blockIdx.x);
     const float sx = x_scale[row];
-    float* y = Y + static_cast<size_t>(row) * N;
-    for (int col = static_cast<int>(blockIdx.y * blockDim.x + threadIdx.x); col < N;
-         col += static_cast<int>(gridDim.y * blockDim.x)) {
-        const int a = __builtin_bit_cast(int, y[col]);
-        float v = static_cast<float>(a) * sx;
-        v = v * w_scale[col];
-        y[col] = v;
-        if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
+    const size_t base = static_cast<size_t>(row) * N;
+    auto one = [&](uint32_t word, float sw, float& y, int& a) {
+        a = static_cast<int>(word);
+        y = static_cast<float>(a) * sx;
+        y = y * sw;
+    };
+    if constexpr (VEC4) {
+        for (int c = static_cast<int>(blockIdx.y * blockDim.x + threadIdx.x); 4 * c < N;
+             c += static_cast<int>(gridDim.y * blockDim.x)) {
+            const uint4 w = *reinterpret_cast<const uint4*>(Y + base + 4 * c);
+            const float4 sw = *reinterpret_cast<const float4*>(w_scale + 4 * c);
+            float4 y;
+            int4 a;
+            one(w.x, sw.x, y.x, a.x);
+            one(w.y, sw.y, y.y, a.y);
+            one(w.z, sw.z, y.z, a.z);
+            one(w.w, sw.w, y.w, a.w);
+            *reinterpret_cast<float4*>(Y + base + 4 * c) = y;
+            if (WRITE_ACC) *reinterpret_cast<int4*>(acc_out + base + 4 * c) = a;
+        }
+    } else {
+        for (int col = static_cast<int>(blockIdx.y * blockDim.x + threadIdx.x); col < N;
+             col += static_cast<int>(gridDim.y * blockDim.x)) {
+            float y;
+            int a;
+            one(__builtin_bit_cast(uint32_t, Y[base + col]), w_scale[col], y, a);
+            Y[base + col] = y;
+            if (WRITE_ACC) acc_out[base + col] = a;
+        }
     }
+}
+
+template <bool WRITE_ACC>
+void launch_dequant(dim3 grid, bool vec4, hipStream_t s, float* Y, const float* x_scale, const float* w_scale,
+                    int N, int32_t* acc_out) {
+    if (vec4)
+        hipLaunchKernelGGL((split_dequant<WRITE_ACC, true>), grid, dim3(256), 0, s, Y, x_scale, w_scale, N, acc_out);
+    else
+        hipLaunchKernelGGL((split_dequant<WRITE_ACC, false>), grid, dim3(256), 0, s, Y, x_scale, w_scale, N, acc_out);
 }
 
 }  // namespace
@@ -121,21 +155,21 @@ hipError_t launch_w4a4_gemm_fp6(const uint8_t* Xq, const float* x_scale, const u
     return hipGetLastError();
 }
 
-// Number of K slices for the split-K form, 0 where it does not apply.  A
-// slice costs about its steps of 128 codes plus two (the pipeline's fill and
-// the epilogue) at kStepUs each, and its atomic additions kAtomicUs per
-// million outputs (measured: 16.8 M no-return int32 atomic additions take
-// about 41 us on MI355X, whatever the contention); the slice count that
-// minimises the sum is taken, among powers of two that keep every slice at
-// two steps or more and all slices in one round of the compute units.
-// AUTO takes it only past the weight-streaming kernel's 128 rows, where the
-// tiles leave at least half of the compute units idle, and when the model
-// (with the fill and dequantizing passes priced at HBM speed) predicts a
-// saving of a sixth or more over one round of whole tiles.
+// Number of K slices for the split-K form, 0 where it does not apply.  The
+// costs are fits to MI355X timings (µs, outputs in millions):
+//   slices       1.35 per step of 128 codes in the longest slice, plus 2.8 per
+//                million atomic int32 additions (slices x outputs; the
+//                additions are bound by their bytes: packing two outputs into
+//                one 64-bit addition measured no faster);
+//   fill + pass  8 + 1.9 per million outputs (two short launches);
+//   whole tiles  16 + 1.17 per step, plus 0.0018 per step and tile (one round
+//                of the int8 or FP6 256 x 256 tiles: the alternative).
+// The slice count is the power of two that minimises the slices' cost while
+// every slice keeps two steps or more and all slices fit in one round of the
+// compute units.  AUTO takes it only past the weight-streaming kernel's 128
+// rows, where the whole tiles leave half of the compute units idle, and when
+// the prediction is at least 5% below the whole tiles'.
 int w4a4_gemm_fp6_split_slices(int M, int N, int K, bool forced) {
-    constexpr double kStepUs = 3500.0 / 2400.0;
-    constexpr double kAtomicUs = 41.0 / 16.8;
-    constexpr double kPassUsPerMillion = 12.0 / 5.0;   // 12 bytes per output at 5 TB/s
     if (M <= 0 || N <= 0 || K % kF6StepCodes != 0 || K < 2 * kF6StepCodes || K > kGemmFp6MaxK) return 0;
     const int cus = device_cu_count();
     if (cus <= 0) return 0;
@@ -143,14 +177,14 @@ int w4a4_gemm_fp6_split_slices(int M, int N, int K, bool forced) {
     if (!forced && (M <= 128 || 2 * tiles > cus)) return 0;
     const int steps = K / kF6StepCodes;
     const double outputs = static_cast<double>(M) * N / 1e6;
-    auto cost = [&](int S) { return ((steps + S - 1) / S + 2) * kStepUs + S * outputs * kAtomicUs; };
+    auto cost = [&](int S) { return 1.35 * ((steps + S - 1) / S) + 2.8 * S * outputs; };
     int best = 1;
     for (int S = 2; steps / S >= 2 && tiles * S <= cus; S *= 2)
         if (cost(S) < cost(best)) best = S;
     if (forced) return best;
-    const double whole = ((tiles + cus - 1) / cus) * (steps + 2) * kStepUs;
-    if (best < 2 || 6.0 * (cost(best) + outputs * kPassUsPerMillion) > 5.0 * whole) return 0;
-    return best;
+    const double whole = 16.0 + 1.17 * steps + 0.0018 * steps * static_cast<double>(tiles);
+    const double split = cost(best) + 8.0 + 1.9 * outputs;
+    return best >= 2 && split < 0.95 * whole ? best : 0;
 }
 
 hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
@@ -161,16 +195,17 @@ hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, c
         return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const size_t n = static_cast<size_t>(M) * N;
-    const unsigned zb = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 8192));
-    hipLaunchKernelGGL(zero_partials, dim3(zb), dim3(256), 0, s, reinterpret_cast<int32_t*>(Y), n);
+    const unsigned zb = static_cast<unsigned>(std::min<size_t>((n / 4 + 255) / 256 + 1, 8192));
+    hipLaunchKernelGGL(zero_partials, dim3(zb), dim3(256), 0, s, reinterpret_cast<uint32_t*>(Y), n);
     const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
     hipLaunchKernelGGL(w4a4_gemm_fp6_split, dim3(static_cast<unsigned>(tiles * slices)), dim3(kF6Threads), 0, s,
                        Xq, Wq, M, N, K, slices, Y);
-    const dim3 fin(static_cast<unsigned>(M), static_cast<unsigned>((N + 1023) / 1024));
+    const bool vec4 = N % 4 == 0;
+    const dim3 fin(static_cast<unsigned>(M), static_cast<unsigned>((N + (vec4 ? 1023 : 255)) / (vec4 ? 1024 : 256)));
     if (acc_out)
-        hipLaunchKernelGGL((split_dequant<true>), fin, dim3(256), 0, s, Y, x_scale, w_scale, N, acc_out);
+        launch_dequant<true>(fin, vec4, s, Y, x_scale, w_scale, N, acc_out);
     else
-        hipLaunchKernelGGL((split_dequant<false>), fin, dim3(256), 0, s, Y, x_scale, w_scale, N, acc_out);
+        launch_dequant<false>(fin, vec4, s, Y, x_scale, w_scale, N, acc_out);
     return hipGetLastError();
 }
 
