@@ -41,6 +41,18 @@ __device__ __forceinline__ void tile_of(int bid, int tilesM, int tilesN, int* tm
     *tn = r / rows;
 }
 
+// After the main loop: once every wave has left it (the first barrier; no
+// stage is read or filled after that), every thread with `has` set stores
+// `v` to word threadIdx.x of the LDS, and the workgroup waits; returns the
+// words as floats.
+__device__ __forceinline__ const float* stage_scales(uint8_t* lds, float v, bool has) {
+    float* sc = reinterpret_cast<float*>(lds);
+    __syncthreads();
+    if (has) sc[threadIdx.x] = v;
+    __syncthreads();
+    return sc;
+}
+
 __device__ __forceinline__ int slot_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 typedef const __attribute__((address_space(3))) void* lds_cptr;

@@ -313,45 +313,74 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
         rotate();
         ++s;
     }
+    // The epilogue's scales, one per thread (x_scale of tile row t for t <
+    // 256, w_scale of tile column t - 256 after), requested two steps before
+    // they are used: loaded in the epilogue, each store waited for its own.
+    float scale = 0.0f;
+    if (!SPLIT)
+        scale = tid < kF6T ? x_scale[min(m0 + tid, M - 1)] : w_scale[min(n0 + tid - kF6T, N - 1)];
     body(s, cur, nxt, dst, P0, P1, false, true);
     rotate();
     body(s + 1, cur, nxt, dst, P0, P1, false, false);
 
     // code sums per operand row (A rows at 0..255, B at 256..511): the two
-    // halves of a row sit in lanes l and l + 32; through the idle first stage
+    // halves of a row sit in lanes l and l + 32; they and the scales go
+    // through the first stage (every stage is idle after the last step's
+    // barrier)
     sumA += __shfl_xor(sumA, 32, 64);
     sumB += __shfl_xor(sumB, 32, 64);
     int* sums = reinterpret_cast<int*>(lds);
+    float* scales = reinterpret_cast<float*>(lds) + 2 * kF6T;
     if (h == 0) {
         sums[r] = sumA;
         sums[kF6T + r] = sumB;
     }
+    if (!SPLIT) scales[tid] = scale;
     barrier_lds();
+    // the accumulators are final here: the last step's MFMAs sunk into the
+    // epilogue would keep their operands live and spill them
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
 
     // epilogue: acc = sum u_a u_b -> exact dot product of the codes, then
     // Y = fl32(fl32(acc * s_x) * s_w).  Result register r of lane l holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 tile.
+    // Everything but the stores runs for every lane (the LDS reads batch).
     const int k64 = 64 * steps * kF6StepCodes;
+    int sb[2];
+    float sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int ct = 64 * wn + 32 * j + (lane & 31);
+        sb[j] = sums[kF6T + ct];
+        sw[j] = SPLIT ? 0.0f : scales[kF6T + ct];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        // the row values of this 32-row block, read before any store
+        int sa[16];
+        float sx[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int rt = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int row = m0 + rt;
-            if (row >= M) continue;
-            const float sx = SPLIT ? 0.0f : x_scale[row];
-            const int sa = sums[rt];
+            sa[r] = sums[rt];
+            sx[r] = SPLIT ? 0.0f : scales[rt];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int ct = 64 * wn + 32 * j + (lane & 31);
-                const int col = n0 + ct;
-                if (col < N) {
-                    const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa + sums[kF6T + ct]) - k64;
+                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+                const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa[r] + sb[j]) - k64;
+                if (row < M && col < N) {
                     if (SPLIT) {
                         atomicAdd(reinterpret_cast<int*>(Y) + static_cast<size_t>(row) * N + col, a);
                     } else {
-                        float y = static_cast<float>(a) * sx;
-                        y = y * w_scale[col];
+                        float y = static_cast<float>(a) * sx[r];
+                        y = y * sw[j];
                         Y[static_cast<size_t>(row) * N + col] = y;
                         if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                     }
@@ -543,36 +572,65 @@ __device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, c
         rotate();
         ++s;
     }
+    // the epilogue's per-row and per-column values, requested two steps
+    // before they are used (as in gemm_tile)
+    float scale;
+    int xsum = 0;
+    if (tid < kF6T) {
+        scale = x_scale[min(m0 + tid, M - 1)];
+        xsum = x_sum[min(m0 + tid, M - 1)];
+    } else {
+        scale = w_scale[min(n0 + tid - kF6T, N - 1)];
+    }
     body(s, cur, nxt, dst, P0, P1, false, true);
     rotate();
     body(s + 1, cur, nxt, dst, P0, P1, false, false);
 
     // weight-code sums per column (the two halves of a row sit in lanes l and
-    // l + 32), through the first stage, idle after the last barrier
+    // l + 32), the activation sums and the scales, through the first stage,
+    // idle after the last barrier: [B sums | A sums | x scales | w scales]
     sumB += __shfl_xor(sumB, 32, 64);
     int* sums = reinterpret_cast<int*>(lds);
+    float* scales = reinterpret_cast<float*>(lds) + 2 * kF6T;
     if (h == 0) sums[r] = sumB;
+    if (tid < kF6T) sums[kF6T + tid] = xsum;
+    scales[tid] = scale;
     barrier_lds();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
 
-    // epilogue as in gemm_tile, the activation sums from x_sum
+    // epilogue as in gemm_tile
     const int k64 = 64 * K;
+    int sb[2];
+    float sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int ct = 64 * wn + 32 * j + (lane & 31);
+        sb[j] = sums[ct];
+        sw[j] = scales[kF6T + ct];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        int sa[16];
+        float sx[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int rt = 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            const int row = m0 + rt;
-            if (row >= M) continue;
-            const float sx = x_scale[row];
-            const int sa = x_sum[row];
+            sa[rr] = sums[kF6T + rt];
+            sx[rr] = scales[rt];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = m0 + 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int ct = 64 * wn + 32 * j + (lane & 31);
-                const int col = n0 + ct;
-                if (col < N) {
-                    const int a = static_cast<int>(acc[i][j][rr]) - 8 * (sa + sums[ct]) - k64;
-                    float y = static_cast<float>(a) * sx;
-                    y = y * w_scale[col];
+                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+                const int a = static_cast<int>(acc[i][j][rr]) - 8 * (sa[rr] + sb[j]) - k64;
+                if (row < M && col < N) {
+                    float y = static_cast<float>(a) * sx[rr];
+                    y = y * sw[j];
                     Y[static_cast<size_t>(row) * N + col] = y;
                     if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                 }

@@ -82,9 +82,16 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
     }
 
     // Output layout of a 16x16 MFMA tile: lane l holds rows 4 * (l / 16) + r,
-    // r = 0..3, of column l % 16.
+    // r = 0..3, of column l % 16.  The scales are loaded ahead of the stores'
+    // branches (inside them every store would wait for its own loads).
+    float sw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sw[j] = w_scale[min(n0 + wn + j * 16 + (lane & 15), N - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float sx[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sx[r] = x_scale[min(m0 + wm + i * 16 + (lane >> 4) * 4 + r, M - 1)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int col = n0 + wn + j * 16 + (lane & 15);
@@ -93,8 +100,8 @@ __global__ __launch_bounds__(256) void w4a4_gemm_basic(
                 const int row = m0 + wm + i * 16 + (lane >> 4) * 4 + r;
                 if (row < M && col < N) {
                     const int a = acc[i][j][r] >> 8;
-                    float y = static_cast<float>(a) * x_scale[row];
-                    y = y * w_scale[col];
+                    float y = static_cast<float>(a) * sx[r];
+                    y = y * sw[j];
                     Y[static_cast<size_t>(row) * N + col] = y;
                     if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                 }
@@ -196,6 +203,11 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < steps) issue(s);
+    // the epilogue's scales, requested now: thread t < 256 takes tile row t,
+    // 256 <= t < 512 tile column t - 256
+    float scale = 0.0f;
+    if (tid < kT) scale = x_scale[min(m0 + tid, M - 1)];
+    else if (tid < 2 * kT) scale = w_scale[min(n0 + tid - kT, N - 1)];
 
     for (int step = 0; step < steps; ++step) {
         // This wave's loads of `step` are done once at most (later steps in
@@ -240,20 +252,24 @@ __global__ __launch_bounds__(kGemmThreads) void w4a4_gemm_256(
         }
     }
 
+    // the tile's scales through LDS (read from global memory in the
+    // epilogue, every store waited for its own two loads)
+    const float* sc = stage_scales(lds, scale, tid < 2 * kT);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+        float sx[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[r] = sc[wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= M) continue;
-            const float sx = x_scale[row];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int col = n0 + wn + j * 32 + (lane & 31);
-                if (col < N) {
-                    const int a = acc[i][j][r] >> 8;
-                    float y = static_cast<float>(a) * sx;
-                    y = y * w_scale[col];
+                const int a = acc[i][j][r] >> 8;
+                float y = static_cast<float>(a) * sx[r];
+                y = y * sc[kT + wn + j * 32 + (lane & 31)];
+                if (row < M && col < N) {
                     Y[static_cast<size_t>(row) * N + col] = y;
                     if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                 }
@@ -388,23 +404,37 @@ __global__ __launch_bounds__(kWThreads) void w4a4_gemm_wide(
         }
     }
 
+    // the tile's 256 row and 384 column scales through LDS (whole tiles: every
+    // index is in range), loaded once here rather than one store at a time
+    {
+        const float v0 = tid < kWTM ? x_scale[m0 + tid] : w_scale[n0 + tid - kWTM];
+        const float v1 = tid < kWTN + kWTM - kWThreads ? w_scale[n0 + kWThreads - kWTM + tid] : 0.0f;
+        float* sc = reinterpret_cast<float*>(lds);
+        __syncthreads();
+        sc[tid] = v0;
+        if (tid < kWTN + kWTM - kWThreads) sc[kWThreads + tid] = v1;
+        __syncthreads();
+    }
+    const float* sc = reinterpret_cast<const float*>(lds);
+    float sw[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) sw[j] = sc[kWTM + wn + j * 32 + (lane & 31)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float sx[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[r] = sc[wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= M) continue;
-            const float sx = x_scale[row];
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 const int col = n0 + wn + j * 32 + (lane & 31);
-                if (col < N) {
-                    const int a = acc[i][j][r] >> 8;
-                    float y = static_cast<float>(a) * sx;
-                    y = y * w_scale[col];
-                    Y[static_cast<size_t>(row) * N + col] = y;
-                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
-                }
+                const int a = acc[i][j][r] >> 8;
+                float y = static_cast<float>(a) * sx[r];
+                y = y * sw[j];
+                Y[static_cast<size_t>(row) * N + col] = y;
+                if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
             }
         }
     }

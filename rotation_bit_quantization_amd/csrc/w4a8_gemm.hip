@@ -126,6 +126,11 @@ __global__ __launch_bounds__(kThreads8) void w4a8_gemm_256(
 #pragma unroll
     for (int s = 0; s < kStages8 - 1; ++s)
         if (s < steps) issue(s);
+    // the epilogue's scales, requested now: thread t < 256 takes tile row t,
+    // 256 <= t < 512 tile column t - 256
+    float scale = 0.0f;
+    if (tid < kT8) scale = x_scale[min(m0 + tid, M - 1)];
+    else if (tid < 2 * kT8) scale = w_scale[min(n0 + tid - kT8, N - 1)];
 
     for (int step = 0; step < steps; ++step) {
         // This wave's loads of `step` are complete once at most the next
@@ -166,20 +171,24 @@ __global__ __launch_bounds__(kThreads8) void w4a8_gemm_256(
         }
     }
 
+    // the tile's scales through LDS (read from global memory in the
+    // epilogue, every store waited for its own two loads)
+    const float* sc = stage_scales(lds, scale, tid < 2 * kT8);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+        float sx[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[r] = sc[wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= M) continue;
-            const float sx = x_scale[row];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int col = n0 + wn + j * 32 + (lane & 31);
-                if (col < N) {
-                    const int a = acc[i][j][r] >> 4;
-                    float y = static_cast<float>(a) * sx;
-                    y = y * w_scale[col];
+                const int a = acc[i][j][r] >> 4;
+                float y = static_cast<float>(a) * sx[r];
+                y = y * sc[kT8 + wn + j * 32 + (lane & 31)];
+                if (row < M && col < N) {
                     Y[static_cast<size_t>(row) * N + col] = y;
                     if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
                 }
