@@ -119,6 +119,71 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
+// The epilogue of a wave's 128 x 64 part of a tile: acc = sum u_a u_b ->
+// the exact dot product of the codes (minus 8 times the row's and the
+// column's code sums and 64 per code), then Y = fl32(fl32(acc * s_x) * s_w),
+// or with SPLIT an atomic int32 addition of acc into Y.  Result register r of
+// lane l of accumulator (i, j) holds tile row 128 wm + 32 i + 8 (r / 4) +
+// 4 (l / 32) + r % 4 and column 64 wn + 32 j + l % 32.  The row and column
+// values come from the LDS (`sums_a`, `sums_b`, `sc_a`, `sc_b`, indexed by
+// tile row and column); they are read in batches of 16 before any store.
+// Tiles inside M and N store without per-element checks, from one address
+// per lane and a wave-uniform row offset.
+template <bool WRITE_ACC, bool SPLIT>
+__device__ __forceinline__ void tile_epilogue(const v16f (&acc)[4][2], const int* sums_a, const int* sums_b,
+                                              const float* sc_a, const float* sc_b, int k64, int M, int N, int m0,
+                                              int n0, int wm, int wn, int lane, float* __restrict__ Y,
+                                              int32_t* __restrict__ acc_out) {
+    const int rl = 128 * wm + 4 * (lane >> 5);   // the lane's first tile row
+    const int cl = 64 * wn + (lane & 31);        // and column
+    int sb[2];
+    float sw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        sb[j] = sums_b[cl + 32 * j];
+        sw[j] = SPLIT ? 0.0f : sc_b[cl + 32 * j];
+    }
+    const size_t lane_off = static_cast<size_t>(m0 + rl) * N + (n0 + cl);
+    auto emit = [&](auto checked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int sa[16];
+            float sx[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rt = rl + 32 * i + 8 * (r >> 2) + (r & 3);
+                sa[r] = sums_a[rt];
+                sx[r] = SPLIT ? 0.0f : sc_a[rt];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
+                const size_t off = lane_off + static_cast<size_t>(ro) * N;
+                const bool row_ok = m0 + rl + ro < M;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa[r] + sb[j]) - k64;
+                    const bool ok = !decltype(checked)::value || (row_ok && n0 + cl + 32 * j < N);
+                    if (SPLIT) {
+                        if (ok) atomicAdd(reinterpret_cast<int*>(Y) + off + 32 * j, a);
+                    } else {
+                        float y = static_cast<float>(a) * sx[r];
+                        y = y * sw[j];
+                        if (ok) {
+                            Y[off + 32 * j] = y;
+                            if (WRITE_ACC) acc_out[off + 32 * j] = a;
+                        }
+                    }
+                }
+            }
+        }
+    };
+    if (m0 + kF6T <= M && n0 + kF6T <= N)
+        emit(std::false_type{});
+    else
+        emit(std::true_type{});
+}
+
 // One 256 x 256 output tile (tm, tn) by the workgroup of kF6Threads threads,
 // on `lds` (three stages of kF6StageBytes, 1024-byte aligned).  Every thread of
 // the workgroup calls it; it returns once the tile's stores are issued, with
@@ -344,50 +409,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ Xq, const 
 #pragma unroll
         for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
 
-    // epilogue: acc = sum u_a u_b -> exact dot product of the codes, then
-    // Y = fl32(fl32(acc * s_x) * s_w).  Result register r of lane l holds row
-    // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 tile.
-    // Everything but the stores runs for every lane (the LDS reads batch).
-    const int k64 = 64 * steps * kF6StepCodes;
-    int sb[2];
-    float sw[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int ct = 64 * wn + 32 * j + (lane & 31);
-        sb[j] = sums[kF6T + ct];
-        sw[j] = SPLIT ? 0.0f : scales[kF6T + ct];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // the row values of this 32-row block, read before any store
-        int sa[16];
-        float sx[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rt = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            sa[r] = sums[rt];
-            sx[r] = SPLIT ? 0.0f : scales[rt];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-                const int a = static_cast<int>(acc[i][j][r]) - 8 * (sa[r] + sb[j]) - k64;
-                if (row < M && col < N) {
-                    if (SPLIT) {
-                        atomicAdd(reinterpret_cast<int*>(Y) + static_cast<size_t>(row) * N + col, a);
-                    } else {
-                        float y = static_cast<float>(a) * sx[r];
-                        y = y * sw[j];
-                        Y[static_cast<size_t>(row) * N + col] = y;
-                        if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
-                    }
-                }
-            }
-        }
-    }
+    tile_epilogue<WRITE_ACC, SPLIT>(acc, sums, sums + kF6T, scales, scales + kF6T, 64 * steps * kF6StepCodes, M, N,
+                                    m0, n0, wm, wn, lane, Y, acc_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,41 +625,8 @@ __device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, c
         for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
 
     // epilogue as in gemm_tile
-    const int k64 = 64 * K;
-    int sb[2];
-    float sw[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int ct = 64 * wn + 32 * j + (lane & 31);
-        sb[j] = sums[ct];
-        sw[j] = scales[kF6T + ct];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int sa[16];
-        float sx[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int rt = 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            sa[rr] = sums[kF6T + rt];
-            sx[rr] = scales[rt];
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = m0 + 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
-                const int a = static_cast<int>(acc[i][j][rr]) - 8 * (sa[rr] + sb[j]) - k64;
-                if (row < M && col < N) {
-                    float y = static_cast<float>(a) * sx[rr];
-                    y = y * sw[j];
-                    Y[static_cast<size_t>(row) * N + col] = y;
-                    if (WRITE_ACC) acc_out[static_cast<size_t>(row) * N + col] = a;
-                }
-            }
-        }
-    }
+    tile_epilogue<WRITE_ACC, false>(acc, sums + kF6T, sums, scales, scales + kF6T, 64 * K, M, N, m0, n0, wm, wn,
+                                    lane, Y, acc_out);
 }
 
 }  // namespace fp6
