@@ -209,6 +209,30 @@ spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const fl
                                               static_cast<hipStream_t>(stream)));
 }
 
+spin_status spin_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream) {
+    if (!Wq || !Wf6 || !w_sum) return SPIN_ERR_NULL;
+    if (N < 0 || K <= 0 || K % 64 != 0 || K > SPIN_GEMM_MAX_K) return SPIN_ERR_BAD_SHAPE;
+    if (!aligned16(Wq) || !aligned16(Wf6) || !aligned16(w_sum)) return SPIN_ERR_MISALIGNED;
+    if (N == 0) return SPIN_OK;
+    return from_hip(spin::launch_weights_f6(Wq, N, K, Wf6, w_sum, static_cast<hipStream_t>(stream)));
+}
+
+spin_status spin_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
+                                const uint8_t* Wf6, const int32_t* w_sum, const float* w_scale, int M, int N,
+                                int K, float* Y, int32_t* acc_out, void* stream) {
+    if (!Xf6 || !x_sum || !x_scale || !Wf6 || !w_sum || !w_scale || !Y) return SPIN_ERR_NULL;
+    if (M < 0 || N < 0 || K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_GEMM_FP6_MAX_K)
+        return SPIN_ERR_BAD_SHAPE;
+    const long long tiles = (static_cast<long long>(M) + 255) / 256 * ((static_cast<long long>(N) + 255) / 256);
+    if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
+    if (!aligned16(Xf6) || !aligned16(x_sum) || !aligned16(x_scale) || !aligned16(Wf6) || !aligned16(w_sum) ||
+        !aligned16(w_scale) || !aligned16(Y) || (acc_out && !aligned16(acc_out)))
+        return SPIN_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return SPIN_OK;
+    return from_hip(spin::launch_w4a4_gemm_f6f6(Xf6, x_sum, x_scale, Wf6, w_sum, w_scale, M, N, K, Y, acc_out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
                           uint8_t* codes, uint16_t* scale, float* X_rot, void* stream) {
     return kv_quant_impl(X, x_dtype, T, H, D, rotate, 4, codes, scale, X_rot, stream);

@@ -629,5 +629,152 @@ __device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, c
                                     lane, Y, acc_out);
 }
 
+// ---------------------------------------------------------------------------
+// gemm_tile_f6ab: both operands already in the FP6 operand layout (the
+// activations from spin_fwht_quant_f6, the weights packed once by
+// spin_weights_f6) with their code sums given.  Every part of a stage is then
+// a contiguous 3 KB piece per 32-row block that one wave copies global -> LDS
+// with the LDS DMA: wave w copies activation block m0 / 32 + w and weight
+// block n0 / 32 + w (the last block for tiles past M or N), six 1 KB copies
+// per step and no conversion at all.  Stage layout as in gemm_tile_f6a.
+template <bool WRITE_ACC>
+__device__ __forceinline__ void gemm_tile_f6ab(const uint8_t* __restrict__ Xf6, const int32_t* __restrict__ x_sum,
+                                               const float* __restrict__ x_scale, const uint8_t* __restrict__ Wf6,
+                                               const int32_t* __restrict__ w_sum, const float* __restrict__ w_scale,
+                                               int M, int N, int K, float* __restrict__ Y,
+                                               int32_t* __restrict__ acc_out, int tm, int tn, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m0 = tm * kF6T, n0 = tn * kF6T;
+    const int steps = K / kF6StepCodes;
+    const int ksteps = K / 64;
+    const uint32_t lds0 = lds_addr(lds);
+
+    const int rba = min(m0 / 32 + wave, (M + 31) / 32 - 1);
+    const int rbb = min(n0 / 32 + wave, (N + 31) / 32 - 1);
+    const uint8_t* srcA = Xf6 + static_cast<size_t>(rba) * ksteps * 1536 + lane * 16;
+    const uint8_t* srcB = Wf6 + static_cast<size_t>(rbb) * ksteps * 1536 + lane * 16;
+    const uint32_t dmaA = lds0 + wave * kF6F6aBlock;          // wave-uniform
+    const uint32_t dmaB = dmaA + kF6F6aHalf;
+    auto dma = [&](int step, uint32_t stage_off) {
+        const size_t o = static_cast<size_t>(step) * 2 * 1536;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            lds_dma16(srcA + o + q * 1024, __builtin_amdgcn_readfirstlane(dmaA + stage_off + q * 1024));
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            lds_dma16(srcB + o + q * 1024, __builtin_amdgcn_readfirstlane(dmaB + stage_off + q * 1024));
+    };
+
+    const int wm = wave >> 2, wn = wave & 3;
+    const uint32_t fr = lds0 + (lane >> 5) * kF6Region + (lane & 31) * 24;
+    uint32_t fbase[6];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fbase[i] = opaque(fr + (4 * wm + i) * kF6F6aBlock);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fbase[4 + j] = opaque(fr + kF6F6aHalf + (2 * wn + j) * kF6F6aBlock);
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    typedef const __attribute__((address_space(3))) uint64_t* lds_u64;
+    auto frag = [&](uint32_t off, int f) {
+        const lds_u64 a = reinterpret_cast<lds_u64>(static_cast<uintptr_t>(fbase[f] + off));
+        const uint64_t x = a[0], y = a[1], z = a[2];
+        const int u = __builtin_nondeterministic_value(0);   // the operand reads six dwords
+        return v8i{static_cast<int>(x), static_cast<int>(x >> 32), static_cast<int>(y), static_cast<int>(y >> 32),
+                   static_cast<int>(z), static_cast<int>(z >> 32), u, u};
+    };
+    v8i fa[4], fbx[2], fby[2];
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    // One step s: the copies of step s + 2 into stage `dst` issued first, the
+    // MFMAs of both k-steps with the next k-step's operands read during the
+    // current one's, the copies waited for, one barrier.
+    auto body = [&](uint32_t cur, uint32_t nxt, uint32_t dst, int copy_step, bool prefetch) {
+        if (copy_step >= 0) dma(copy_step, dst);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            v8i* fb = ks == 0 ? fbx : fby;
+            v8i* fbn = ks == 0 ? fby : fbx;
+            const uint32_t noff = ks == 0 ? cur + kF6Region * 2 : nxt;
+            const bool more = ks == 0 || prefetch;
+            if (more) {
+                fbn[0] = frag(noff, 4);
+                fbn[1] = frag(noff, 5);
+            }
+            fence();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[0], acc[i][0], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[1], acc[i][1], 2, 2, 0,
+                                                                          kF6Scale, 0, kF6Scale);
+                if (more) fa[i] = frag(noff, i);
+                fence();
+            }
+        }
+        if (copy_step >= 0) SPIN_WAIT_VMCNT(0);
+        barrier_lds();
+    };
+
+    // prologue: steps 0 and 1 into stages 0 and 1, the operands of step 0's
+    // first k-step read
+    dma(0, 0);
+    dma(min(1, steps - 1), kF6StageBytes);
+    SPIN_WAIT_VMCNT(0);
+    barrier_lds();
+    fbx[0] = frag(0, 4);
+    fbx[1] = frag(0, 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(0, i);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every body starts with no LDS access in flight
+
+    uint32_t cur = 0, nxt = kF6StageBytes, dst = 2 * kF6StageBytes;
+    auto rotate = [&] {
+        const uint32_t t = cur;
+        cur = nxt;
+        nxt = dst;
+        dst = t;
+    };
+    int s = 0;
+    for (; s + 2 < steps; ++s) {
+        body(cur, nxt, dst, s + 2, true);
+        rotate();
+    }
+    // the epilogue's per-row and per-column values (as in gemm_tile)
+    float scale;
+    int sum;
+    if (tid < kF6T) {
+        scale = x_scale[min(m0 + tid, M - 1)];
+        sum = x_sum[min(m0 + tid, M - 1)];
+    } else {
+        scale = w_scale[min(n0 + tid - kF6T, N - 1)];
+        sum = w_sum[min(n0 + tid - kF6T, N - 1)];
+    }
+    body(cur, nxt, dst, -1, true);
+    rotate();
+    body(cur, nxt, dst, -1, false);
+
+    // [A sums | B sums | x scales | w scales] through the first stage, idle
+    // after the last barrier
+    int* sums = reinterpret_cast<int*>(lds);
+    float* scales = reinterpret_cast<float*>(lds) + 2 * kF6T;
+    sums[tid] = sum;
+    scales[tid] = scale;
+    barrier_lds();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
+    tile_epilogue<WRITE_ACC, false>(acc, sums, sums + kF6T, scales, scales + kF6T, 64 * K, M, N, m0, n0, wm, wn,
+                                    lane, Y, acc_out);
+}
+
 }  // namespace fp6
 }  // namespace spin

@@ -32,6 +32,46 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6a(
     gemm_tile_f6a<WRITE_ACC>(Xf6, x_sum, x_scale, Wq, w_scale, M, N, K, Y, acc_out, tm, tn, lds);
 }
 
+template <bool WRITE_ACC>
+__global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6ab(
+    const uint8_t* __restrict__ Xf6, const int32_t* __restrict__ x_sum, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ Wf6, const int32_t* __restrict__ w_sum, const float* __restrict__ w_scale, int M,
+    int N, int K, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kF6StageBytes];
+    int tm, tn;
+    tile_of(blockIdx.x, (M + kF6T - 1) / kF6T, (N + kF6T - 1) / kF6T, &tm, &tn);
+    gemm_tile_f6ab<WRITE_ACC>(Xf6, x_sum, x_scale, Wf6, w_sum, w_scale, M, N, K, Y, acc_out, tm, tn, lds);
+}
+
+// Packed weight codes [N][K/2] -> the FP6 operand layout (the conversion the
+// tiles apply to 16-byte chunks, so that the fields and their order are the
+// ones the tiles would have written to their stages) and the code sum of
+// every row.  Workgroup n takes row n; thread t its 32-code chunks t, t + 256, ...
+__global__ __launch_bounds__(256) void weights_f6_kernel(const uint8_t* __restrict__ Wq, int K,
+                                                         uint8_t* __restrict__ Wf6, int32_t* __restrict__ w_sum) {
+    const int n = static_cast<int>(blockIdx.x);
+    const int chunks = K / 32;
+    const size_t ksteps = static_cast<size_t>(K) / 64;
+    uint8_t* block = Wf6 + static_cast<size_t>(n / 32) * ksteps * 1536 + (n % 32) * 24;
+    int sum = 0;
+    for (int c = static_cast<int>(threadIdx.x); c < chunks; c += 256) {
+        const uint4 q = *reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(n) * (K / 2) + 16 * c);
+        uint32_t o[6];
+        chunk_to_fp6(q, o, sum);
+        uint2* d = reinterpret_cast<uint2*>(block + static_cast<size_t>(c / 2) * 1536 + (c % 2) * 768);
+        d[0] = make_uint2(o[0], o[1]);
+        d[1] = make_uint2(o[2], o[3]);
+        d[2] = make_uint2(o[4], o[5]);
+    }
+    // workgroup sum: within each wave, then across the four waves
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    __shared__ int part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) w_sum[n] = part[0] + part[1] + part[2] + part[3];
+}
+
 // Split-K: block b takes K slice `sl` of one tile.  Blocks are put in an
 // order in which each XCD holds a contiguous range of (slice, tile) pairs,
 // the tiles of one slice column-major (the few row blocks of a column share
@@ -206,6 +246,27 @@ hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, c
         launch_dequant<true>(fin, vec4, s, Y, x_scale, w_scale, N, acc_out);
     else
         launch_dequant<false>(fin, vec4, s, Y, x_scale, w_scale, N, acc_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s) {
+    if (N <= 0 || K % 64 != 0 || K <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(weights_f6_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, s, Wq, K, Wf6, w_sum);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
+                                 const uint8_t* Wf6, const int32_t* w_sum, const float* w_scale, int M, int N, int K,
+                                 float* Y, int32_t* acc_out, hipStream_t s) {
+    if (K % kF6StepCodes != 0 || K < 2 * kF6StepCodes || K > kGemmFp6MaxK) return hipErrorInvalidValue;
+    const long long tiles = static_cast<long long>((M + kF6T - 1) / kF6T) * ((N + kF6T - 1) / kF6T);
+    const dim3 grid(static_cast<unsigned>(tiles));
+    if (acc_out)
+        hipLaunchKernelGGL((w4a4_gemm_fp6_f6ab<true>), grid, dim3(kF6Threads), 0, s, Xf6, x_sum, x_scale, Wf6, w_sum,
+                           w_scale, M, N, K, Y, acc_out);
+    else
+        hipLaunchKernelGGL((w4a4_gemm_fp6_f6ab<false>), grid, dim3(kF6Threads), 0, s, Xf6, x_sum, x_scale, Wf6,
+                           w_sum, w_scale, M, N, K, Y, acc_out);
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
            "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6", "spin_w4a4_gemm_f6",
-           "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6", "SPIN_GEMM_FP6_SPLITK",
+           "spin_weights_f6", "spin_w4a4_gemm_f6f6", "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6", "SPIN_GEMM_FP6_SPLITK",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
@@ -31,7 +31,7 @@ SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                     "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
                     "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6",
-                    "spin_w4a4_gemm_f6",
+                    "spin_w4a4_gemm_f6", "spin_weights_f6", "spin_w4a4_gemm_f6f6",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +70,8 @@ def load():
     lib.spin_fwht_quant_gemm_noalloc.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp]
     lib.spin_fwht_quant_f6.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a4_gemm_f6.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.spin_weights_f6.argtypes = [vp, i, i, vp, vp, vp]
+    lib.spin_w4a4_gemm_f6f6.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a8_gemm.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
@@ -251,6 +253,46 @@ def spin_w4a4_gemm_f6(Xf6, x_sum, x_scale, Wq, w_scale, Y=None, acc_out=None, wa
     st = load().spin_w4a4_gemm_f6(_ptr(Xf6), _ptr(x_sum), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K,
                                   _ptr(Y), _ptr(acc_out), _stream(stream))
     _raise("spin_w4a4_gemm_f6", st)
+    return Y, acc_out
+
+
+def spin_weights_f6(Wq, Wf6=None, w_sum=None, stream=None):
+    """Packed Wq [N, K/2] -> (Wf6 uint8 [f6_bytes(N, K)], w_sum [N] int32): the weight codes in the
+    FP6 operand layout, for spin_w4a4_gemm_f6f6."""
+    _check(Wq, "Wq", (torch.uint8,))
+    N, Kh = Wq.shape
+    K = 2 * Kh
+    dev = Wq.device
+    Wf6 = torch.empty((f6_bytes(N, K),), dtype=torch.uint8, device=dev) if Wf6 is None else Wf6
+    w_sum = torch.empty((N,), dtype=torch.int32, device=dev) if w_sum is None else w_sum
+    _check(Wf6, "Wf6", (torch.uint8,), (f6_bytes(N, K),))
+    _check(w_sum, "w_sum", (torch.int32,), (N,))
+    st = load().spin_weights_f6(_ptr(Wq), N, K, _ptr(Wf6), _ptr(w_sum), _stream(stream))
+    _raise("spin_weights_f6", st)
+    return Wf6, w_sum
+
+
+def spin_w4a4_gemm_f6f6(Xf6, x_sum, x_scale, Wf6, w_sum, w_scale, K, Y=None, acc_out=None, want_acc=False,
+                        stream=None):
+    """Both operands in the FP6 operand layout (+ code sums, scales) -> (Y [M, N] fp32, acc [M, N] int32
+    or None).  K is the reduction length (the layouts do not carry it)."""
+    _check(x_sum, "x_sum", (torch.int32,))
+    _check(w_sum, "w_sum", (torch.int32,))
+    M, N = x_sum.shape[0], w_sum.shape[0]
+    _check(Xf6, "Xf6", (torch.uint8,), (f6_bytes(M, K),))
+    _check(Wf6, "Wf6", (torch.uint8,), (f6_bytes(N, K),))
+    _check(x_scale, "x_scale", (torch.float32,), (M,))
+    _check(w_scale, "w_scale", (torch.float32,), (N,))
+    dev = Wf6.device
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev) if Y is None else Y
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _check(Y, "Y", (torch.float32,), (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", (torch.int32,), (M, N))
+    st = load().spin_w4a4_gemm_f6f6(_ptr(Xf6), _ptr(x_sum), _ptr(x_scale), _ptr(Wf6), _ptr(w_sum), _ptr(w_scale),
+                                    M, N, K, _ptr(Y), _ptr(acc_out), _stream(stream))
+    _raise("spin_w4a4_gemm_f6f6", st)
     return Y, acc_out
 
 

@@ -261,6 +261,37 @@ def test_f6_pair_validation(lib):
     assert g6(M=0) == spin.SPIN_OK and g6(N=0) == spin.SPIN_OK
 
 
+def test_f6_weights_validation(lib):
+    f = lib.spin_weights_f6
+
+    def w6(w=A, N=4, K=12288, wf=A, wsum=A):
+        return f(w, N, K, wf, wsum, None)
+
+    for name in ("w", "wf", "wsum"):
+        assert w6(**{name: None}) == spin.SPIN_ERR_NULL, name
+        assert w6(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert w6(K=0) == spin.SPIN_ERR_BAD_SHAPE
+    assert w6(K=96) == spin.SPIN_ERR_BAD_SHAPE
+    assert w6(K=171136 + 64) == spin.SPIN_ERR_BAD_SHAPE
+    assert w6(N=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert w6(N=0) == spin.SPIN_OK
+
+    g = lib.spin_w4a4_gemm_f6f6
+
+    def g66(xf=A, xsum=A, xs=A, wf=A, wsum=A, ws_=A, M=4, N=4, K=12288, y=A, acc=None):
+        return g(xf, xsum, xs, wf, wsum, ws_, M, N, K, y, acc, None)
+
+    for name in ("xf", "xsum", "xs", "wf", "wsum", "ws_", "y"):
+        assert g66(**{name: None}) == spin.SPIN_ERR_NULL, name
+    for name in ("xf", "xsum", "xs", "wf", "wsum", "ws_", "y", "acc"):
+        assert g66(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
+    assert g66(K=128) == spin.SPIN_ERR_BAD_SHAPE
+    assert g66(K=8192 + 64) == spin.SPIN_ERR_BAD_SHAPE
+    assert g66(K=65536 + 128) == spin.SPIN_ERR_BAD_SHAPE
+    assert g66(N=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert g66(M=0) == spin.SPIN_OK and g66(N=0) == spin.SPIN_OK
+
+
 def test_kv_qkv_validation(lib):
     f = lib.spin_kv_qkv
 

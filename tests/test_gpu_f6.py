@@ -118,3 +118,77 @@ def test_down_proj_step_f6_full_size():
     Y6, acc6 = spin.spin_w4a4_gemm_f6(Xf6, xsum, xs6, Wq, ws, want_acc=True)
     assert np.array_equal(_host(acc6), _host(acc))
     assert np.array_equal(_host(Y6).view(np.uint32), _host(Y).view(np.uint32))
+
+
+# ---------------------------------------------------------------- weights in the FP6 layout too
+
+@pytest.mark.parametrize("N,K", [(1, 64), (37, 256), (300, 4096), (4096 + 5, 12288)])
+def test_weights_f6_is_the_layout_of_the_codes(N, K):
+    """spin_weights_f6 writes the weight codes in the FP6 operand layout (decoded
+    by the host decoder written from the layout's definition) and their row sums."""
+    rng = np.random.default_rng(N + K)
+    qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    Wf6, wsum = spin.spin_weights_f6(_dev(oracle.pack_int4(qw)))
+    assert np.array_equal(f6_layout.decode(_host(Wf6), N, K), qw)
+    assert np.array_equal(_host(wsum), qw.astype(np.int64).sum(axis=1))
+
+
+def check_gemm_f6f6(qx, qw, sx, sw, rows=None):
+    M, K = qx.shape
+    Xf6 = _dev(f6_layout.encode(qx))
+    xsum = _dev(qx.astype(np.int64).sum(axis=1).astype(np.int32))
+    Wq = _dev(oracle.pack_int4(qw))
+    Wf6, wsum = spin.spin_weights_f6(Wq)
+    Y, acc = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, _dev(sx), Wf6, wsum, _dev(sw), K, want_acc=True)
+    y, a = _host(Y), _host(acc)
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    a_ref = oracle.gemm_rows(qx, qw, sel)
+    assert np.array_equal(a[sel].astype(np.int64), a_ref)
+    assert np.array_equal(y[sel], oracle.dequant(a_ref, sx[sel], sw))
+    Y2, acc2 = spin.spin_w4a4_gemm(_dev(oracle.pack_int4(qx)), _dev(sx), Wq, _dev(sw), want_acc=True)
+    assert np.array_equal(_host(acc2), a) and np.array_equal(_host(Y2).view(np.uint32), y.view(np.uint32))
+    Y3, _ = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, _dev(sx), Wf6, wsum, _dev(sw), K)
+    assert np.array_equal(_host(Y3).view(np.uint32), y.view(np.uint32))
+    return y, a
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (37, 53, 384), (40, 70, 640), (300, 200, 8192),
+                                   (257, 300, 12288), (4096 + 37, 259, 12288), (1000, 1030, 8320)])
+def test_gemm_f6f6_ragged(M, N, K):
+    """Both operands copied into the stages: ragged tiles (the last 32-row
+    blocks of both operands hold padding), the shortest pipelines (two and
+    three steps) and odd step counts."""
+    rng = np.random.default_rng(M * 5 + N + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sx = rng.random(M).astype(np.float32)
+    sw = (rng.random(N) * 0.01).astype(np.float32)
+    check_gemm_f6f6(qx, qw, sx, sw)
+
+
+def test_gemm_f6f6_largest_k_extremes():
+    """K = 65536 with every code at +-7 and -8 nibbles."""
+    K, M, N = 65536, 20, 7
+    rng = np.random.default_rng(K + 2)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    qx[0], qx[1], qx[2] = 7, -7, -8
+    qw[0], qw[1], qw[2] = 7, -7, -8
+    _, a = check_gemm_f6f6(qx, qw, np.ones(M, np.float32), np.ones(N, np.float32))
+    assert a[0, 0] == 49 * K and a[1, 0] == -49 * K and a[0, 1] == -49 * K
+    assert a[2, 2] == 64 * K and a[2, 0] == -56 * K
+
+
+def test_down_proj_step_f6f6_full_size():
+    """The down_proj workload with both operands in the FP6 layout equals the
+    nibble path bit for bit."""
+    cfg = synth.down_config()
+    X = _dev(cfg["x"])
+    _, Wq, ws = spin.spin_fold_rotation(_dev(cfg["w"]), None, 12288)
+    Xq, xs, _ = spin.spin_fwht_quant(X, 12288)
+    Y, acc = spin.spin_w4a4_gemm(Xq, xs, Wq, ws, want_acc=True)
+    Xf6, xsum, xs6 = spin.spin_fwht_quant_f6(X)
+    Wf6, wsum = spin.spin_weights_f6(Wq)
+    Y6, acc6 = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, xs6, Wf6, wsum, ws, 12288, want_acc=True)
+    assert np.array_equal(_host(acc6), _host(acc))
+    assert np.array_equal(_host(Y6).view(np.uint32), _host(Y).view(np.uint32))
