@@ -344,11 +344,27 @@ def extra_workloads(args, dev, stream):
     t_q = _time(lambda i: spin.spin_fwht_quant(X[i % sets], 1, Xq=Xq[i % sets], x_scale=xs[i % sets]), reps, stream)
     t_g = _time(lambda i: spin.spin_w4a4_gemm(Xq[i % sets], xs[i % sets], Wq[i % sets], ws, Y=Y[i % sets]), reps,
                 stream)
+    # the same GEMM with both operands in the FP6 operand layout: the weights
+    # packed once (offline, untimed), the activation codes rewritten by
+    # spin_codes_f6 after the quantizer (timed)
+    f6w = [spin.spin_codes_f6(w) for w in Wq]
+    f6x = [spin.spin_codes_f6(x) for x in Xq]
+    for i in range(args.warmup):
+        j = i % sets
+        spin.spin_w4a4_gemm_f6f6(f6x[j][0], f6x[j][1], xs[j], f6w[j][0], f6w[j][1], ws, 4096, Y=Y[j])
+    t_c = _time(lambda i: spin.spin_codes_f6(Xq[i % sets], f6x[i % sets][0], f6x[i % sets][1]), reps, stream)
+    t_g6 = _time(lambda i: spin.spin_w4a4_gemm_f6f6(f6x[i % sets][0], f6x[i % sets][1], xs[i % sets],
+                                                    f6w[i % sets][0], f6w[i % sets][1], ws, 4096, Y=Y[i % sets]),
+                 reps, stream)
+    ops = 2.0 * 4096 * 6144 * 4096
     out["qkv_proj"] = {"workload": "X 4096x4096 fp16 quant-only, W 4096x6144 (R1 4096 folded), M=4096",
                        "quant_us": t_q * 1e3, "gemm_us": t_g * 1e3,
-                       "gemm_tops": 2.0 * 4096 * 6144 * 4096 / (t_g * 1e-3) / 1e12,
-                       "gemm_frac_of_int8_peak": 2.0 * 4096 * 6144 * 4096 / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS}
-    del X, Xq, xs, Y, Wq, ws
+                       "gemm_tops": ops / (t_g * 1e-3) / 1e12,
+                       "gemm_frac_of_int8_peak": ops / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                       "codes_f6_us": t_c * 1e3, "gemm_f6f6_us": t_g6 * 1e3,
+                       "gemm_f6f6_tops": ops / (t_g6 * 1e-3) / 1e12,
+                       "gemm_f6f6_frac_of_int8_peak": ops / (t_g6 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    del X, Xq, xs, Y, Wq, ws, f6w, f6x
 
     # decoder-layer chain: qkv, o_proj (R2 128), gate/up (2 x 12288), down (H_12288)
     c = synth.chain_config(M=8192)
@@ -595,7 +611,43 @@ def main():
                         "spin_fwht_quant_f6 (4096 x 12288 fp16, H_12288) + spin_w4a4_gemm_f6 (4096 x 4096 x 12288)",
             "fwht_quant_f6_us": f6_us, "gemm_f6_us": g6_us, "gemm_f6_tops": gemm_ops / g6_us / 1e6,
             "step_us": f6_us + g6_us}
-        del Xf6, xsum
+
+        # ... and with the weights too in the FP6 operand layout, packed once
+        # (spin_codes_f6, offline, untimed): spin_w4a4_gemm_f6f6
+        Wf6, wsum = spin.spin_codes_f6(Wq)
+
+        def step66(i, ev=None):
+            j = i % sets
+            if ev is not None:
+                he.record(ev[0], stream)
+            spin.spin_fwht_quant_f6(X[j], Xf6=Xf6[j], x_sum=xsum[j], x_scale=xs[j])
+            if ev is not None:
+                he.record(ev[1], stream)
+            spin.spin_w4a4_gemm_f6f6(Xf6[j], xsum[j], xs[j], Wf6, wsum, ws, K, Y=Y[j])
+            if ev is not None:
+                he.record(ev[2], stream)
+
+        for i in range(args.warmup):
+            step66(i)
+        torch.cuda.synchronize()
+        ev66 = [[he.new() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step66(i, ev66[i])
+        torch.cuda.synchronize()
+        f66_us = float(np.mean([he.ms(e[0], e[1]) for e in ev66])) * 1e3
+        g66 = [he.ms(e[1], e[2]) * 1e3 for e in ev66]
+        g66_us = float(np.mean(g66))
+        he.release()
+        g66_tops = gemm_ops / g66_us / 1e6
+        extra["down_proj_f6f6"] = {
+            "workload": "the down_proj step with both operands in the FP6 operand layout: spin_fwht_quant_f6 "
+                        "(4096 x 12288 fp16, H_12288) + spin_w4a4_gemm_f6f6 (4096 x 4096 x 12288), the weights "
+                        "packed once by spin_codes_f6 (offline, untimed)",
+            "fwht_quant_f6_us": f66_us, "gemm_f6f6_us": g66_us, "gemm_f6f6_median_us": float(np.median(g66)),
+            "step_us": f66_us + g66_us,
+            "roofline_gemm_f6f6": {"kernel": "w4a4_gemm_fp6_f6ab", "bound": "mfma", "achieved": g66_tops,
+                                   "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": g66_tops / INT8_PEAK_TOPS}}
+        del Xf6, xsum, Wf6, wsum
 
     if not args.no_fused:
         # The same step as one launch (spin_fwht_quant_gemm) against the two calls,

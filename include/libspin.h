@@ -168,7 +168,7 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
 /*
  * The FP6 operand layout of activation codes, written by spin_fwht_quant_f6
  * and read by spin_w4a4_gemm_f6 and spin_w4a4_gemm_f6f6 (this library's
- * format, also that of spin_weights_f6's weight codes; the pages fix no
+ * format, also written by spin_codes_f6; the pages fix no
  * storage): the INT4 codes q of an [M][K] activation matrix, each held as the
  * 6-bit field of u = q + 8 (bits 0..3 = u, bits 4..5 = 0: the FP6 E2M3 value
  * u / 8), ordered for the gfx950 matrix cores.  Row r, code k lies in the
@@ -213,26 +213,28 @@ spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const fl
                               int32_t* acc_out, void* stream);
 
 /*
- * spin_weights_f6 — packed weight codes (spin_fold_rotation's Wq) rewritten
- * once, offline, in the FP6 operand layout above (the layout of a [N][K] code
- * matrix: weight row n in place of activation row r), with the code sum of
- * every row, for spin_w4a4_gemm_f6f6.  Abstract: W4A4; the weights are static,
- * so their conversion to the matrix cores' operand format leaves the hot path.
+ * spin_codes_f6 — packed INT4 codes [R][K/2] (spin_fold_rotation's Wq, or
+ * the activation codes of spin_fwht_quant) rewritten in the FP6 operand
+ * layout above (row n of the code matrix in place of row r), with the code
+ * sum of every row, for spin_w4a4_gemm_f6f6.  Weights are static, so theirs
+ * is done once, offline (abstract: W4A4), and the conversion of the weight
+ * codes into the matrix cores' operand format leaves the hot path.
  *
  *   Wq     [N][K/2] uint8    packed codes
  *   Wf6    SPIN_F6_BYTES(N, K) bytes   OUTPUT (padding rows past N unwritten)
- *   w_sum  [N] int32         OUTPUT: sum_k qw[n][k]
+ *   w_sum  [N] int32         OUTPUT: sum_k q[n][k]
  * Requirements: N >= 0, K > 0, K % 64 == 0, K <= SPIN_GEMM_MAX_K.
  */
-spin_status spin_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream);
+spin_status spin_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream);
 
 /*
  * spin_w4a4_gemm_f6f6 — spin_w4a4_gemm with both operands in the FP6 operand
- * layout (activations from spin_fwht_quant_f6, weights from spin_weights_f6):
+ * layout (activations from spin_fwht_quant_f6, weights from spin_codes_f6):
  * Y and acc_out are the same bits spin_w4a4_gemm gives for those codes.
  *
  *   Xf6, x_sum, x_scale   as for spin_w4a4_gemm_f6
- *   Wf6      SPIN_F6_BYTES(N, K) bytes, w_sum [N] int32 (from spin_weights_f6)
+ *   Wf6      SPIN_F6_BYTES(N, K) bytes, w_sum [N] int32 (the weight codes
+ *            from spin_codes_f6)
  *   w_scale, Y, acc_out   as for spin_w4a4_gemm
  * Requirements: M, N >= 0, K % 128 == 0,
  * SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K.

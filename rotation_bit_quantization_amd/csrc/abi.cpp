@@ -209,12 +209,12 @@ spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const fl
                                               static_cast<hipStream_t>(stream)));
 }
 
-spin_status spin_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream) {
+spin_status spin_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream) {
     if (!Wq || !Wf6 || !w_sum) return SPIN_ERR_NULL;
     if (N < 0 || K <= 0 || K % 64 != 0 || K > SPIN_GEMM_MAX_K) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(Wq) || !aligned16(Wf6) || !aligned16(w_sum)) return SPIN_ERR_MISALIGNED;
     if (N == 0) return SPIN_OK;
-    return from_hip(spin::launch_weights_f6(Wq, N, K, Wf6, w_sum, static_cast<hipStream_t>(stream)));
+    return from_hip(spin::launch_codes_f6(Wq, N, K, Wf6, w_sum, static_cast<hipStream_t>(stream)));
 }
 
 spin_status spin_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,

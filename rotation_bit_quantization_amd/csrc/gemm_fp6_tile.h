@@ -632,7 +632,7 @@ __device__ __forceinline__ void gemm_tile_f6a(const uint8_t* __restrict__ Xf6, c
 // ---------------------------------------------------------------------------
 // gemm_tile_f6ab: both operands already in the FP6 operand layout (the
 // activations from spin_fwht_quant_f6, the weights packed once by
-// spin_weights_f6) with their code sums given.  Every part of a stage is then
+// spin_codes_f6) with their code sums given.  Every part of a stage is then
 // a contiguous 3 KB piece per 32-row block that one wave copies global -> LDS
 // with the LDS DMA: wave w copies activation block m0 / 32 + w and weight
 // block n0 / 32 + w (the last block for tiles past M or N), six 1 KB copies

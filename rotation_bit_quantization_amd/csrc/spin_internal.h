@@ -40,7 +40,7 @@ int w4a4_gemm_fp6_split_slices(int M, int N, int K, bool forced);
 hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq,
                                       const float* w_scale, int M, int N, int K, int slices, float* Y,
                                       int32_t* acc_out, hipStream_t s);
-hipError_t launch_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s);
+hipError_t launch_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s);
 hipError_t launch_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
                                  const uint8_t* Wf6, const int32_t* w_sum, const float* w_scale, int M, int N, int K,
                                  float* Y, int32_t* acc_out, hipStream_t s);

@@ -43,11 +43,11 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6ab(
     gemm_tile_f6ab<WRITE_ACC>(Xf6, x_sum, x_scale, Wf6, w_sum, w_scale, M, N, K, Y, acc_out, tm, tn, lds);
 }
 
-// Packed weight codes [N][K/2] -> the FP6 operand layout (the conversion the
+// Packed codes [N][K/2] -> the FP6 operand layout (the conversion the
 // tiles apply to 16-byte chunks, so that the fields and their order are the
 // ones the tiles would have written to their stages) and the code sum of
 // every row.  Workgroup n takes row n; thread t its 32-code chunks t, t + 256, ...
-__global__ __launch_bounds__(256) void weights_f6_kernel(const uint8_t* __restrict__ Wq, int K,
+__global__ __launch_bounds__(256) void codes_f6_kernel(const uint8_t* __restrict__ Wq, int K,
                                                          uint8_t* __restrict__ Wf6, int32_t* __restrict__ w_sum) {
     const int n = static_cast<int>(blockIdx.x);
     const int chunks = K / 32;
@@ -249,9 +249,9 @@ hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, c
     return hipGetLastError();
 }
 
-hipError_t launch_weights_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s) {
+hipError_t launch_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s) {
     if (N <= 0 || K % 64 != 0 || K <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(weights_f6_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, s, Wq, K, Wf6, w_sum);
+    hipLaunchKernelGGL(codes_f6_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, s, Wq, K, Wf6, w_sum);
     return hipGetLastError();
 }
 

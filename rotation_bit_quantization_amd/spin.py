@@ -19,7 +19,7 @@ __all__ = ["SpinError", "load", "library_path", "SPIN_OK", "SPIN_ERR_NULL",
            "SPIN_F32", "SPIN_F16", "spin_status_string", "spin_fold_rotation", "spin_fwht_quant",
            "spin_w4a4_gemm", "spin_kv_quant", "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8",
            "spin_kv_qkv", "spin_w4a4_gemm_ex", "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6", "spin_w4a4_gemm_f6",
-           "spin_weights_f6", "spin_w4a4_gemm_f6f6", "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6", "SPIN_GEMM_FP6_SPLITK",
+           "spin_codes_f6", "spin_w4a4_gemm_f6f6", "f6_bytes", "SPIN_GEMM_AUTO", "SPIN_GEMM_INT8", "SPIN_GEMM_FP6", "SPIN_GEMM_FP6_SPLITK",
            "EXPORTED_SYMBOLS"]
 
 SPIN_OK, SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED, SPIN_ERR_UNSUPPORTED, \
@@ -31,7 +31,7 @@ SPIN_FWHT_QUANT_GEMM_WORKSPACE_WORDS = 1025
 EXPORTED_SYMBOLS = ("spin_fold_rotation", "spin_fwht_quant", "spin_w4a4_gemm", "spin_kv_quant",
                     "spin_fwht_quant8", "spin_w4a8_gemm", "spin_kv_quant8", "spin_kv_qkv", "spin_w4a4_gemm_ex",
                     "spin_fwht_quant_gemm", "spin_fwht_quant_gemm_noalloc", "spin_fwht_quant_f6",
-                    "spin_w4a4_gemm_f6", "spin_weights_f6", "spin_w4a4_gemm_f6f6",
+                    "spin_w4a4_gemm_f6", "spin_codes_f6", "spin_w4a4_gemm_f6f6",
                     "spin_status_string", "spin_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,7 +70,7 @@ def load():
     lib.spin_fwht_quant_gemm_noalloc.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp]
     lib.spin_fwht_quant_f6.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
     lib.spin_w4a4_gemm_f6.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
-    lib.spin_weights_f6.argtypes = [vp, i, i, vp, vp, vp]
+    lib.spin_codes_f6.argtypes = [vp, i, i, vp, vp, vp]
     lib.spin_w4a4_gemm_f6f6.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.spin_kv_quant.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp]
     lib.spin_fwht_quant8.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
@@ -256,9 +256,9 @@ def spin_w4a4_gemm_f6(Xf6, x_sum, x_scale, Wq, w_scale, Y=None, acc_out=None, wa
     return Y, acc_out
 
 
-def spin_weights_f6(Wq, Wf6=None, w_sum=None, stream=None):
-    """Packed Wq [N, K/2] -> (Wf6 uint8 [f6_bytes(N, K)], w_sum [N] int32): the weight codes in the
-    FP6 operand layout, for spin_w4a4_gemm_f6f6."""
+def spin_codes_f6(Wq, Wf6=None, w_sum=None, stream=None):
+    """Packed codes [N, K/2] (weights, or activations) -> (uint8 [f6_bytes(N, K)], row sums [N] int32):
+    the codes in the FP6 operand layout, for spin_w4a4_gemm_f6f6."""
     _check(Wq, "Wq", (torch.uint8,))
     N, Kh = Wq.shape
     K = 2 * Kh
@@ -267,8 +267,8 @@ def spin_weights_f6(Wq, Wf6=None, w_sum=None, stream=None):
     w_sum = torch.empty((N,), dtype=torch.int32, device=dev) if w_sum is None else w_sum
     _check(Wf6, "Wf6", (torch.uint8,), (f6_bytes(N, K),))
     _check(w_sum, "w_sum", (torch.int32,), (N,))
-    st = load().spin_weights_f6(_ptr(Wq), N, K, _ptr(Wf6), _ptr(w_sum), _stream(stream))
-    _raise("spin_weights_f6", st)
+    st = load().spin_codes_f6(_ptr(Wq), N, K, _ptr(Wf6), _ptr(w_sum), _stream(stream))
+    _raise("spin_codes_f6", st)
     return Wf6, w_sum
 
 

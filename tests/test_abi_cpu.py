@@ -261,8 +261,8 @@ def test_f6_pair_validation(lib):
     assert g6(M=0) == spin.SPIN_OK and g6(N=0) == spin.SPIN_OK
 
 
-def test_f6_weights_validation(lib):
-    f = lib.spin_weights_f6
+def test_codes_f6_validation(lib):
+    f = lib.spin_codes_f6
 
     def w6(w=A, N=4, K=12288, wf=A, wsum=A):
         return f(w, N, K, wf, wsum, None)

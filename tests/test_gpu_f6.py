@@ -123,12 +123,12 @@ def test_down_proj_step_f6_full_size():
 # ---------------------------------------------------------------- weights in the FP6 layout too
 
 @pytest.mark.parametrize("N,K", [(1, 64), (37, 256), (300, 4096), (4096 + 5, 12288)])
-def test_weights_f6_is_the_layout_of_the_codes(N, K):
-    """spin_weights_f6 writes the weight codes in the FP6 operand layout (decoded
+def test_codes_f6_is_the_layout_of_the_codes(N, K):
+    """spin_codes_f6 writes the weight codes in the FP6 operand layout (decoded
     by the host decoder written from the layout's definition) and their row sums."""
     rng = np.random.default_rng(N + K)
     qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
-    Wf6, wsum = spin.spin_weights_f6(_dev(oracle.pack_int4(qw)))
+    Wf6, wsum = spin.spin_codes_f6(_dev(oracle.pack_int4(qw)))
     assert np.array_equal(f6_layout.decode(_host(Wf6), N, K), qw)
     assert np.array_equal(_host(wsum), qw.astype(np.int64).sum(axis=1))
 
@@ -138,7 +138,7 @@ def check_gemm_f6f6(qx, qw, sx, sw, rows=None):
     Xf6 = _dev(f6_layout.encode(qx))
     xsum = _dev(qx.astype(np.int64).sum(axis=1).astype(np.int32))
     Wq = _dev(oracle.pack_int4(qw))
-    Wf6, wsum = spin.spin_weights_f6(Wq)
+    Wf6, wsum = spin.spin_codes_f6(Wq)
     Y, acc = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, _dev(sx), Wf6, wsum, _dev(sw), K, want_acc=True)
     y, a = _host(Y), _host(acc)
     sel = np.arange(M) if rows is None else np.asarray(rows)
@@ -188,7 +188,7 @@ def test_down_proj_step_f6f6_full_size():
     Xq, xs, _ = spin.spin_fwht_quant(X, 12288)
     Y, acc = spin.spin_w4a4_gemm(Xq, xs, Wq, ws, want_acc=True)
     Xf6, xsum, xs6 = spin.spin_fwht_quant_f6(X)
-    Wf6, wsum = spin.spin_weights_f6(Wq)
+    Wf6, wsum = spin.spin_codes_f6(Wq)
     Y6, acc6 = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, xs6, Wf6, wsum, ws, 12288, want_acc=True)
     assert np.array_equal(_host(acc6), _host(acc))
     assert np.array_equal(_host(Y6).view(np.uint32), _host(Y).view(np.uint32))
