@@ -397,6 +397,36 @@ def extra_workloads(args, dev, stream):
                           "us": t8 * 1e3, "tops": ops / (t8 * 1e-3) / 1e12,
                           "frac_of_int8_peak": ops / (t8 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
 
+    # the same chain with both GEMM operands in the FP6 operand layout: the
+    # weights packed once by spin_codes_f6 (offline, untimed); the down_proj
+    # input through spin_fwht_quant_f6, the others quantized and rewritten by
+    # spin_codes_f6 (timed)
+    for L in layers:
+        L["wf6"] = spin.spin_codes_f6(L["wq"][0])
+        L["xf6"] = torch.empty((spin.f6_bytes(8192, L["K"]),), dtype=torch.uint8, device=dev)
+        L["xsum"] = torch.empty((8192,), dtype=torch.int32, device=dev)
+
+    def chain6():
+        for L in layers:
+            if L["had_n"] == HAD_N:
+                spin.spin_fwht_quant_f6(L["x"], Xf6=L["xf6"], x_sum=L["xsum"], x_scale=L["sc"])
+            else:
+                xq, _, _ = spin.spin_fwht_quant(L["x"], L["had_n"], Xq=L["xq"], x_scale=L["sc"])
+                spin.spin_codes_f6(xq, L["xf6"], L["xsum"])
+            spin.spin_w4a4_gemm_f6f6(L["xf6"], L["xsum"], L["sc"], L["wf6"][0], L["wf6"][1], L["ws"][0], L["K"],
+                                     Y=L["y"])
+
+    for _ in range(2):
+        chain6()
+    t86 = _time(lambda i: chain6(), max(3, reps // 3), stream)
+    out["chain_m8192_f6f6"] = {"workload": "the same chain at M=8192 with both GEMM operands in the FP6 operand "
+                                           "layout (weights packed offline; activation codes rewritten by "
+                                           "spin_codes_f6 or written by spin_fwht_quant_f6, timed)",
+                               "us": t86 * 1e3, "tops": ops / (t86 * 1e-3) / 1e12,
+                               "frac_of_int8_peak": ops / (t86 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    for L in layers:
+        del L["wf6"], L["xf6"], L["xsum"]
+
     # decode, M = 16: weight bytes dominate; four weight copies rotate so they come from HBM
     for L in layers:
         for _ in range(3):

@@ -46,15 +46,18 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6ab(
 // Packed codes [N][K/2] -> the FP6 operand layout (the conversion the
 // tiles apply to 16-byte chunks, so that the fields and their order are the
 // ones the tiles would have written to their stages) and the code sum of
-// every row.  Workgroup n takes row n; thread t its 32-code chunks t, t + 256, ...
-__global__ __launch_bounds__(256) void codes_f6_kernel(const uint8_t* __restrict__ Wq, int K,
-                                                         uint8_t* __restrict__ Wf6, int32_t* __restrict__ w_sum) {
-    const int n = static_cast<int>(blockIdx.x);
+// every row.  One wave per row (four rows per workgroup of 256): lane l takes
+// the row's 32-code chunks l, l + 64, ...; the sum is reduced across the wave.
+__global__ __launch_bounds__(256) void codes_f6_kernel(const uint8_t* __restrict__ Wq, int N, int K,
+                                                       uint8_t* __restrict__ Wf6, int32_t* __restrict__ w_sum) {
+    const int n = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
+    if (n >= N) return;
+    const int lane = static_cast<int>(threadIdx.x & 63);
     const int chunks = K / 32;
     const size_t ksteps = static_cast<size_t>(K) / 64;
     uint8_t* block = Wf6 + static_cast<size_t>(n / 32) * ksteps * 1536 + (n % 32) * 24;
     int sum = 0;
-    for (int c = static_cast<int>(threadIdx.x); c < chunks; c += 256) {
+    for (int c = lane; c < chunks; c += 64) {
         const uint4 q = *reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(n) * (K / 2) + 16 * c);
         uint32_t o[6];
         chunk_to_fp6(q, o, sum);
@@ -63,13 +66,9 @@ __global__ __launch_bounds__(256) void codes_f6_kernel(const uint8_t* __restrict
         d[1] = make_uint2(o[2], o[3]);
         d[2] = make_uint2(o[4], o[5]);
     }
-    // workgroup sum: within each wave, then across the four waves
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-    __shared__ int part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) w_sum[n] = part[0] + part[1] + part[2] + part[3];
+    if (lane == 0) w_sum[n] = sum;
 }
 
 // Split-K: block b takes K slice `sl` of one tile.  Blocks are put in an
@@ -251,7 +250,8 @@ hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, c
 
 hipError_t launch_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s) {
     if (N <= 0 || K % 64 != 0 || K <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(codes_f6_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, s, Wq, K, Wf6, w_sum);
+    hipLaunchKernelGGL(codes_f6_kernel, dim3(static_cast<unsigned>((N + 3) / 4)), dim3(256), 0, s, Wq, N, K, Wf6,
+                       w_sum);
     return hipGetLastError();
 }
 
