@@ -50,10 +50,10 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 
 # Measured HBM traffic per launch (bytes read, bytes written) from two
 # rocprofv3 passes (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) over
-# `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-fused --no-f6
+# `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-fused
 # --copy-calibration`.
 # Each counter is scaled by what it reads for a 1 GiB device-to-device copy in
-# the same run: FETCH_SIZE reported 524325.69 KiB (factor 2.0), WRITE_SIZE
+# the same run: FETCH_SIZE reported 524325.38 KiB (factor 2.0), WRITE_SIZE
 # 1048576 KiB (factor 1.0).  A figure holds only for the kernel code it was
 # taken on (SHA-256 prefixes of the sources without comments, below); after
 # any change to that code it reports null.
@@ -61,13 +61,16 @@ CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
     "fwht_quant": {"sources": {"fwht_quant.hip": "534a39ba359043de", "fwht12288.h": "aeebefa0ba05bd5b",
                               "spin_device.h": "cf499208765bf25d"},
-                  "read": 101768439, "write": 25296931},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "3844c69f6b0ec334", "w4a4_gemm_fp6.hip": "801edcccc16247f8",
-                              "gemm_fp6_tile.h": "6802538dc64b3645", "gemm_common.h": "0d5f030ce5ed28cd",
+                  "read": 101778345, "write": 25296944},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "3844c69f6b0ec334", "w4a4_gemm_fp6.hip": "515a3aed1456651a",
+                              "gemm_fp6_tile.h": "935c1f9d3fce0dba", "gemm_common.h": "0d5f030ce5ed28cd",
                               "spin_device.h": "cf499208765bf25d"},
-                 "read": 151408242, "write": 67108864},
+                 "read": 151345872, "write": 67108864},
+    "w4a4_gemm_f6f6": {"sources": {"w4a4_gemm_fp6.hip": "515a3aed1456651a", "gemm_fp6_tile.h": "935c1f9d3fce0dba",
+                                   "gemm_common.h": "0d5f030ce5ed28cd", "spin_device.h": "cf499208765bf25d"},
+                      "read": 226868545, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "cf499208765bf25d"},
-                "read": 33640370, "write": 8650752},
+                "read": 33640390, "write": 8650752},
 }
 
 
@@ -676,7 +679,8 @@ def main():
             "fwht_quant_f6_us": f66_us, "gemm_f6f6_us": g66_us, "gemm_f6f6_median_us": float(np.median(g66)),
             "step_us": f66_us + g66_us,
             "roofline_gemm_f6f6": {"kernel": "w4a4_gemm_fp6_f6ab", "bound": "mfma", "achieved": g66_tops,
-                                   "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": g66_tops / INT8_PEAK_TOPS}}
+                                   "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": g66_tops / INT8_PEAK_TOPS,
+                                   "traffic": traffic("w4a4_gemm_f6f6")}}
         del Xf6, xsum, Wf6, wsum
 
     if not args.no_fused:
