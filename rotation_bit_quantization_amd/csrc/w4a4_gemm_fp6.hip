@@ -46,29 +46,46 @@ __global__ __launch_bounds__(kF6Threads) void w4a4_gemm_fp6_f6ab(
 // Packed codes [N][K/2] -> the FP6 operand layout (the conversion the
 // tiles apply to 16-byte chunks, so that the fields and their order are the
 // ones the tiles would have written to their stages) and the code sum of
-// every row.  One wave per row (four rows per workgroup of 256): lane l takes
-// the row's 32-code chunks l, l + 64, ...; the sum is reduced across the wave.
-__global__ __launch_bounds__(256) void codes_f6_kernel(const uint8_t* __restrict__ Wq, int N, int K,
+// every row.  Workgroup b takes the 32-row block b; its sixteen waves split
+// the block's 64-code k-steps in sixteen.  For each k-step lane l converts k-half
+// l / 32 of row l % 32, so that the wave writes the step's 1536-byte region
+// whole; the row sums are reduced in the LDS.  Rows past N are not written.
+constexpr int kCodesWaves = 16;
+
+__global__ __launch_bounds__(64 * kCodesWaves) void codes_f6_kernel(const uint8_t* __restrict__ Wq, int N, int K,
                                                        uint8_t* __restrict__ Wf6, int32_t* __restrict__ w_sum) {
-    const int n = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
-    if (n >= N) return;
-    const int lane = static_cast<int>(threadIdx.x & 63);
-    const int chunks = K / 32;
-    const size_t ksteps = static_cast<size_t>(K) / 64;
-    uint8_t* block = Wf6 + static_cast<size_t>(n / 32) * ksteps * 1536 + (n % 32) * 24;
+    const int blk = static_cast<int>(blockIdx.x);
+    const int wave = static_cast<int>(threadIdx.x >> 6), lane = static_cast<int>(threadIdx.x & 63);
+    const int r = lane & 31, h = lane >> 5;
+    const int row = 32 * blk + r;
+    const bool live = row < N;
+    const int ksteps = K / 64;
+    const int k0 = wave * ksteps / kCodesWaves, k1 = (wave + 1) * ksteps / kCodesWaves;
+    const uint8_t* src = Wq + static_cast<size_t>(live ? row : 0) * (K / 2) + 16 * h;
+    uint8_t* dst = Wf6 + static_cast<size_t>(blk) * ksteps * 1536 + h * 768 + r * 24;
     int sum = 0;
-    for (int c = lane; c < chunks; c += 64) {
-        const uint4 q = *reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(n) * (K / 2) + 16 * c);
+#pragma unroll 4
+    for (int ks = k0; ks < k1; ++ks) {
+        const uint4 q = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(ks) * 32);
         uint32_t o[6];
         chunk_to_fp6(q, o, sum);
-        uint2* d = reinterpret_cast<uint2*>(block + static_cast<size_t>(c / 2) * 1536 + (c % 2) * 768);
-        d[0] = make_uint2(o[0], o[1]);
-        d[1] = make_uint2(o[2], o[3]);
-        d[2] = make_uint2(o[4], o[5]);
+        if (live) {
+            uint2* d = reinterpret_cast<uint2*>(dst + static_cast<size_t>(ks) * 1536);
+            d[0] = make_uint2(o[0], o[1]);
+            d[1] = make_uint2(o[2], o[3]);
+            d[2] = make_uint2(o[4], o[5]);
+        }
     }
+    sum += __shfl_xor(sum, 32, 64);   // the row's two k-halves
+    __shared__ int part[kCodesWaves][32];
+    if (h == 0) part[wave][r] = sum;
+    __syncthreads();
+    if (threadIdx.x < 32 && 32 * blk + static_cast<int>(threadIdx.x) < N) {
+        int t = 0;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-    if (lane == 0) w_sum[n] = sum;
+        for (int w = 0; w < kCodesWaves; ++w) t += part[w][threadIdx.x];
+        w_sum[32 * blk + threadIdx.x] = t;
+    }
 }
 
 // Split-K: block b takes K slice `sl` of one tile.  Blocks are put in an
@@ -250,8 +267,8 @@ hipError_t launch_w4a4_gemm_fp6_split(const uint8_t* Xq, const float* x_scale, c
 
 hipError_t launch_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, hipStream_t s) {
     if (N <= 0 || K % 64 != 0 || K <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(codes_f6_kernel, dim3(static_cast<unsigned>((N + 3) / 4)), dim3(256), 0, s, Wq, N, K, Wf6,
-                       w_sum);
+    hipLaunchKernelGGL(codes_f6_kernel, dim3(static_cast<unsigned>((N + 31) / 32)), dim3(64 * kCodesWaves), 0, s, Wq,
+                       N, K, Wf6, w_sum);
     return hipGetLastError();
 }
 
