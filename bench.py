@@ -786,6 +786,9 @@ def main():
                                     "achieved": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12, 2),
                                     "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-op/s",
                                     "frac": round(M * K * FWHT_VALU_OPS_PER_ELEMENT / f_s / 1e12 / VALU_PEAK_TOPS, 4)},
+        # the same product with both operands in the FP6 operand layout (weights
+        # packed offline): extra.down_proj_f6f6, repeated here for visibility
+        "roofline_w4a4_gemm_f6f6": (extra.get("down_proj_f6f6") or {}).get("roofline_gemm_f6f6"),
         "launch_us": {name: {"mean": round(float(v.mean()) * 1e3, 3), "median": round(float(np.median(v)) * 1e3, 3),
                              "p10": round(float(np.percentile(v, 10)) * 1e3, 3),
                              "p90": round(float(np.percentile(v, 90)) * 1e3, 3)}
