@@ -53,7 +53,7 @@ KV_BYTES_PER_GROUP = 2 * KV_D + KV_D // 2 + 2      # fp16 in + packed codes + fp
 # `bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-fused
 # --copy-calibration`.
 # Each counter is scaled by what it reads for a 1 GiB device-to-device copy in
-# the same run: FETCH_SIZE reported 524325.38 KiB (factor 2.0), WRITE_SIZE
+# the same run: FETCH_SIZE reported 524326.5 KiB (factor 2.0), WRITE_SIZE
 # 1048576 KiB (factor 1.0).  A figure holds only for the kernel code it was
 # taken on (SHA-256 prefixes of the sources without comments, below); after
 # any change to that code it reports null.
@@ -61,16 +61,16 @@ CSRC = os.path.join(ROOT, "rotation_bit_quantization_amd", "csrc")
 TRAFFIC = {
     "fwht_quant": {"sources": {"fwht_quant.hip": "534a39ba359043de", "fwht12288.h": "aeebefa0ba05bd5b",
                               "spin_device.h": "cf499208765bf25d"},
-                  "read": 101778345, "write": 25296944},
-    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "3844c69f6b0ec334", "w4a4_gemm_fp6.hip": "515a3aed1456651a",
+                  "read": 101783406, "write": 25296984},
+    "w4a4_gemm": {"sources": {"w4a4_gemm.hip": "3844c69f6b0ec334", "w4a4_gemm_fp6.hip": "135e165e956c950d",
                               "gemm_fp6_tile.h": "935c1f9d3fce0dba", "gemm_common.h": "0d5f030ce5ed28cd",
                               "spin_device.h": "cf499208765bf25d"},
-                 "read": 151345872, "write": 67108864},
-    "w4a4_gemm_f6f6": {"sources": {"w4a4_gemm_fp6.hip": "515a3aed1456651a", "gemm_fp6_tile.h": "935c1f9d3fce0dba",
+                 "read": 151337580, "write": 67108864},
+    "w4a4_gemm_f6f6": {"sources": {"w4a4_gemm_fp6.hip": "135e165e956c950d", "gemm_fp6_tile.h": "935c1f9d3fce0dba",
                                    "gemm_common.h": "0d5f030ce5ed28cd", "spin_device.h": "cf499208765bf25d"},
-                      "read": 226868545, "write": 67108864},
+                      "read": 227252450, "write": 67108864},
     "kv_quant": {"sources": {"kv_quant.hip": "72f25f38e706d384", "spin_device.h": "cf499208765bf25d"},
-                "read": 33640390, "write": 8650752},
+                "read": 33640465, "write": 8650752},
 }
 
 
