@@ -213,17 +213,21 @@ spin_status spin_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const fl
                               int32_t* acc_out, void* stream);
 
 /*
- * spin_codes_f6 — packed INT4 codes [R][K/2] (spin_fold_rotation's Wq, or
+ * spin_codes_f6 — packed INT4 codes [N][K/2] (spin_fold_rotation's Wq, or
  * the activation codes of spin_fwht_quant) rewritten in the FP6 operand
- * layout above (row n of the code matrix in place of row r), with the code
+ * layout above (row n of the codes as row r of the layout), with the code
  * sum of every row, for spin_w4a4_gemm_f6f6.  Weights are static, so theirs
  * is done once, offline (abstract: W4A4), and the conversion of the weight
- * codes into the matrix cores' operand format leaves the hot path.
+ * codes into the matrix cores' operand format leaves the hot path.  Any
+ * nibble is accepted (-8 becomes the field of u = 0).
  *
  *   Wq     [N][K/2] uint8    packed codes
  *   Wf6    SPIN_F6_BYTES(N, K) bytes   OUTPUT (padding rows past N unwritten)
  *   w_sum  [N] int32         OUTPUT: sum_k q[n][k]
  * Requirements: N >= 0, K > 0, K % 64 == 0, K <= SPIN_GEMM_MAX_K.
+ * Errors: SPIN_ERR_NULL for a null pointer, SPIN_ERR_BAD_SHAPE, and
+ * SPIN_ERR_MISALIGNED unless every pointer is 16-byte aligned; N == 0 enqueues
+ * nothing.
  */
 spin_status spin_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t* w_sum, void* stream);
 
@@ -238,6 +242,9 @@ spin_status spin_codes_f6(const uint8_t* Wq, int N, int K, uint8_t* Wf6, int32_t
  *   w_scale, Y, acc_out   as for spin_w4a4_gemm
  * Requirements: M, N >= 0, K % 128 == 0,
  * SPIN_GEMM_FP6_MIN_K <= K <= SPIN_GEMM_FP6_MAX_K.
+ * Errors: SPIN_ERR_NULL, SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED (16-byte
+ * alignment of every pointer) as for spin_w4a4_gemm_f6; M == 0 or N == 0
+ * enqueues nothing.
  */
 spin_status spin_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale,
                                 const uint8_t* Wf6, const int32_t* w_sum, const float* w_scale, int M, int N,
