@@ -272,7 +272,11 @@ spin_status spin_w4a4_gemm_f6f6(const uint8_t* Xf6, const int32_t* x_sum, const 
  * cooperatively (all its workgroups resident at once).
  * Errors: SPIN_ERR_UNSUPPORTED for another dtype or order, SPIN_ERR_BAD_SHAPE,
  * SPIN_ERR_NULL, SPIN_ERR_MISALIGNED as for the two calls; SPIN_ERR_HIP if
- * the device cannot run the cooperative launch.
+ * the device cannot run the cooperative launch.  The wait of a GEMM tile for
+ * its rows is bounded (about half a second, or 2^22 polls); it cannot expire
+ * while every workgroup is resident, which the cooperative launch ensures,
+ * but if it did, that tile's Y would be written as NaN (acc_out INT32_MIN)
+ * rather than the kernel hanging.
  */
 spin_status spin_fwht_quant_gemm(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
                                  const uint8_t* Wq, const float* w_scale, int N, uint8_t* Xq,
