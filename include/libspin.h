@@ -67,6 +67,12 @@ enum { SPIN_F32 = 0, SPIN_F16 = 1 };
 
 /* Largest row length spin_fwht_quant accepts. */
 #define SPIN_FWHT_MAX_K 32768
+/* Most rows one spin_fwht_quant (and _f6, _gemm) call takes, and most
+   (token, head) vectors one spin_kv_quant call takes: each kernel launch has
+   fewer than 2^32 work-items in its one grid dimension, and these kernels
+   give a row 256 of them, a workgroup of 256 to 32 KV vectors. */
+#define SPIN_FWHT_MAX_M ((1 << 24) - 1)
+#define SPIN_KV_MAX_VECTORS (((1LL << 24) - 1) * 32)
 /* Largest K spin_w4a4_gemm accepts: 49 * K * 256 must stay below 2^31
    (the kernel accumulates codes scaled by 16 on each side in int32). */
 #define SPIN_GEMM_MAX_K 171136
@@ -107,7 +113,8 @@ spin_status spin_fold_rotation(const float* W, int K, int N, const float* R, int
  * y = x . blockdiag(H_n / sqrt(n)) computed in float32 (within 1e-5 relative
  * per row of the exact product); codes are clamp(rne(fl32(y / s)), -7, 7)
  * with the IEEE float32 quotient, bit-exact; a zero row gets s = 0 and zero
- * codes.  Requirements: M >= 0, 0 < K <= SPIN_FWHT_MAX_K, K % 32 == 0.
+ * codes.  Requirements: 0 <= M <= SPIN_FWHT_MAX_M, 0 < K <= SPIN_FWHT_MAX_K,
+ * K % 32 == 0.
  */
 spin_status spin_fwht_quant(const void* X, spin_dtype x_dtype, int M, int K, int had_n,
                             uint8_t* Xq, float* x_scale, float* X_rot, void* stream);
@@ -316,7 +323,7 @@ spin_status spin_fwht_quant_gemm_noalloc(const void* X, spin_dtype x_dtype, int 
  *   X_rot   [T][H][D] float32 or NULL   OUTPUT: the float32 values y
  * codes and scale are both NULL or both non-NULL; when both are NULL, X_rot
  * must be non-NULL (rotate-only, used for Q).  Requirements: T, H >= 0,
- * D == 128, rotate in {0, 1}.
+ * T * H <= SPIN_KV_MAX_VECTORS, D == 128, rotate in {0, 1}.
  */
 spin_status spin_kv_quant(const void* X, spin_dtype x_dtype, int T, int H, int D, int rotate,
                           uint8_t* codes, uint16_t* scale, float* X_rot, void* stream);
@@ -394,7 +401,8 @@ spin_status spin_kv_quant8(const void* X, spin_dtype x_dtype, int T, int H, int 
  * D == 128, bits in {4, 8}; K, V and the four K / V outputs non-NULL.
  * Errors: SPIN_ERR_NULL for a missing pointer or a Q / Q_rot pair with one
  * NULL, SPIN_ERR_UNSUPPORTED for a dtype or bits value outside the above,
- * SPIN_ERR_BAD_SHAPE for a size out of range (T * Hkv or T * Hq above 2^34),
+ * SPIN_ERR_BAD_SHAPE for a size out of range (2 ceil(T Hkv / 32) + ceil(T Hq / 32)
+ * workgroups of 256 above 2^24 - 1, i.e. more than one launch can hold),
  * SPIN_ERR_MISALIGNED as for every call.
  */
 spin_status spin_kv_qkv(const void* Q, const void* K, const void* V, spin_dtype x_dtype, int T, int Hq,

@@ -46,7 +46,7 @@ spin_status fwht_quant_impl(const void* X, spin_dtype x_dtype, int M, int K, int
     if (x_dtype != SPIN_F32 && x_dtype != SPIN_F16) return SPIN_ERR_UNSUPPORTED;
     spin::HadOrder h;
     if (!parse_had(had_n, &h)) return SPIN_ERR_UNSUPPORTED;
-    if (M < 0 || K <= 0 || K > SPIN_FWHT_MAX_K || K % 32 != 0 || K % had_n != 0)
+    if (M < 0 || M > SPIN_FWHT_MAX_M || K <= 0 || K > SPIN_FWHT_MAX_K || K % 32 != 0 || K % had_n != 0)
         return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(X) || !aligned16(Xq) || !aligned16(x_scale) || (X_rot && !aligned16(X_rot)))
         return SPIN_ERR_MISALIGNED;
@@ -63,7 +63,7 @@ spin_status kv_quant_impl(const void* X, spin_dtype x_dtype, int T, int H, int D
     if (x_dtype != SPIN_F32 && x_dtype != SPIN_F16) return SPIN_ERR_UNSUPPORTED;
     if (rotate != 0 && rotate != 1) return SPIN_ERR_UNSUPPORTED;
     if (T < 0 || H < 0 || D != 128) return SPIN_ERR_BAD_SHAPE;
-    if (static_cast<long long>(T) * H > (1LL << 34)) return SPIN_ERR_BAD_SHAPE;
+    if (static_cast<long long>(T) * H > SPIN_KV_MAX_VECTORS) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(X) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
         (X_rot && !aligned16(X_rot)))
         return SPIN_ERR_MISALIGNED;
@@ -80,7 +80,7 @@ spin_status fwht_quant_gemm_impl(const void* X, spin_dtype x_dtype, int M, int K
                                  int32_t* acc_out, uint32_t* workspace, void* stream) {
     if (!X || !Wq || !w_scale || !Xq || !x_scale || !Y) return SPIN_ERR_NULL;
     if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
-    if (K != 12288 || M < 0 || N < 0) return SPIN_ERR_BAD_SHAPE;
+    if (K != 12288 || M < 0 || M > SPIN_FWHT_MAX_M || N < 0) return SPIN_ERR_BAD_SHAPE;
     const long long tiles = (static_cast<long long>(M) + 255) / 256 * ((static_cast<long long>(N) + 255) / 256);
     if (tiles > 0x7FFFFFFFLL) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Xq) || !aligned16(x_scale) ||
@@ -186,7 +186,7 @@ spin_status spin_fwht_quant_f6(const void* X, spin_dtype x_dtype, int M, int K, 
                                int32_t* x_sum, float* x_scale, void* stream) {
     if (!X || !Xf6 || !x_sum || !x_scale) return SPIN_ERR_NULL;
     if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
-    if (K != 12288 || M < 0) return SPIN_ERR_BAD_SHAPE;
+    if (K != 12288 || M < 0 || M > SPIN_FWHT_MAX_M) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(X) || !aligned16(Xf6) || !aligned16(x_sum) || !aligned16(x_scale)) return SPIN_ERR_MISALIGNED;
     if (M == 0) return SPIN_OK;
     return from_hip(spin::launch_fwht_quant_f6(static_cast<const __half*>(X), M, Xf6, x_sum, x_scale,
@@ -252,8 +252,10 @@ spin_status spin_kv_qkv(const void* Q, const void* K, const void* V, spin_dtype 
     if (x_dtype != SPIN_F32 && x_dtype != SPIN_F16) return SPIN_ERR_UNSUPPORTED;
     if (bits != 4 && bits != 8) return SPIN_ERR_UNSUPPORTED;
     if (T < 0 || Hkv < 0 || (Q && Hq < 0) || D != 128) return SPIN_ERR_BAD_SHAPE;
-    if (static_cast<long long>(T) * Hkv > (1LL << 34)) return SPIN_ERR_BAD_SHAPE;
-    if (Q && static_cast<long long>(T) * Hq > (1LL << 34)) return SPIN_ERR_BAD_SHAPE;
+    {   // the one launch's workgroups: K and V 32 vectors each, then Q (as launch_kv_qkv counts them)
+        const long long gkv = static_cast<long long>(T) * Hkv, gq = Q ? static_cast<long long>(T) * Hq : 0;
+        if (2 * ((gkv + 31) / 32) + (gq + 31) / 32 > (1LL << 24) - 1) return SPIN_ERR_BAD_SHAPE;
+    }
     if ((Q && (!aligned16(Q) || !aligned16(Q_rot))) || !aligned16(K) || !aligned16(V) || !aligned16(K_codes) ||
         !aligned16(K_scale) || (K_rot && !aligned16(K_rot)) || !aligned16(V_codes) || !aligned16(V_scale))
         return SPIN_ERR_MISALIGNED;

@@ -64,6 +64,8 @@ def test_fwht_quant_validation(lib):
     assert call(K=48, n=1) == spin.SPIN_ERR_BAD_SHAPE          # K % 32
     assert call(K=512 + 32, n=256) == spin.SPIN_ERR_BAD_SHAPE   # K % had_n
     assert call(K=65536, n=1) == spin.SPIN_ERR_BAD_SHAPE        # above SPIN_FWHT_MAX_K
+    assert call(M=1 << 24) == spin.SPIN_ERR_BAD_SHAPE           # above SPIN_FWHT_MAX_M: one launch's rows
+    assert call(M=(1 << 31) - 1, K=32, n=32) == spin.SPIN_ERR_BAD_SHAPE
     assert call(X=U) == spin.SPIN_ERR_MISALIGNED
     assert call(r=U) == spin.SPIN_ERR_MISALIGNED
     assert call(M=0) == spin.SPIN_OK                             # empty: nothing enqueued
@@ -99,6 +101,10 @@ def test_kv_validation(lib):
     assert call(rot=2) == spin.SPIN_ERR_UNSUPPORTED
     assert call(D=64) == spin.SPIN_ERR_BAD_SHAPE
     assert call(T=-1) == spin.SPIN_ERR_BAD_SHAPE
+    # SPIN_KV_MAX_VECTORS = (2^24 - 1) * 32: 32 past it, one past it, far past it
+    assert call(T=1 << 24, H=32) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(T=((1 << 24) - 1) * 32 + 1, H=1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(T=1 << 30, H=1 << 4) == spin.SPIN_ERR_BAD_SHAPE
     assert call(s=U) == spin.SPIN_ERR_MISALIGNED
     assert call(T=0) == spin.SPIN_OK
 
@@ -205,6 +211,7 @@ def test_fwht_quant_gemm_validation(lib):
     assert call(had=4096) == spin.SPIN_ERR_UNSUPPORTED
     assert call(K=4096) == spin.SPIN_ERR_BAD_SHAPE
     assert call(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert call(M=1 << 24) == spin.SPIN_ERR_BAD_SHAPE
     assert call(N=-1) == spin.SPIN_ERR_BAD_SHAPE
     for name in ("X", "w", "ws_", "xq", "xs", "y", "acc", "work"):
         assert call(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
@@ -243,6 +250,7 @@ def test_f6_pair_validation(lib):
     assert q6(had=4096) == spin.SPIN_ERR_UNSUPPORTED
     assert q6(K=4096) == spin.SPIN_ERR_BAD_SHAPE
     assert q6(M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(M=1 << 24) == spin.SPIN_ERR_BAD_SHAPE
     assert q6(M=0) == spin.SPIN_OK
 
     g = lib.spin_w4a4_gemm_f6
@@ -311,6 +319,9 @@ def test_kv_qkv_validation(lib):
     assert call(Hq=-1) == spin.SPIN_ERR_BAD_SHAPE
     assert call(T=1 << 30, Hkv=32) == spin.SPIN_ERR_BAD_SHAPE   # 2^35 vectors
     assert call(T=1 << 30, Hkv=1, Hq=32) == spin.SPIN_ERR_BAD_SHAPE
+    # the one launch holds 2 ceil(T Hkv / 32) + ceil(T Hq / 32) < 2^24 workgroups
+    assert call(T=1 << 20, Hkv=128, Hq=256) == spin.SPIN_ERR_BAD_SHAPE      # exactly 2^24
+    assert call(T=1 << 23, Hkv=32, Q=None, qr=None) == spin.SPIN_ERR_BAD_SHAPE
     for name in ("Q", "K", "V", "qr", "kc", "ks", "kr", "vc", "vs"):
         assert call(**{name: U}) == spin.SPIN_ERR_MISALIGNED, name
     # Hq is ignored without Q; empty problems enqueue nothing
