@@ -354,8 +354,11 @@ def extra_workloads(args, dev, stream):
     f6x = [spin.spin_codes_f6(x) for x in Xq]
     for i in range(args.warmup):
         j = i % sets
+        spin.spin_fwht_quant_f6(X[j], Xf6=f6x[j][0], x_sum=f6x[j][1], x_scale=xs[j], had_n=1)
         spin.spin_w4a4_gemm_f6f6(f6x[j][0], f6x[j][1], xs[j], f6w[j][0], f6w[j][1], ws, 4096, Y=Y[j])
     t_c = _time(lambda i: spin.spin_codes_f6(Xq[i % sets], f6x[i % sets][0], f6x[i % sets][1]), reps, stream)
+    t_q6 = _time(lambda i: spin.spin_fwht_quant_f6(X[i % sets], Xf6=f6x[i % sets][0], x_sum=f6x[i % sets][1],
+                                                   x_scale=xs[i % sets], had_n=1), reps, stream)
     t_g6 = _time(lambda i: spin.spin_w4a4_gemm_f6f6(f6x[i % sets][0], f6x[i % sets][1], xs[i % sets],
                                                     f6w[i % sets][0], f6w[i % sets][1], ws, 4096, Y=Y[i % sets]),
                  reps, stream)
@@ -364,7 +367,8 @@ def extra_workloads(args, dev, stream):
                        "quant_us": t_q * 1e3, "gemm_us": t_g * 1e3,
                        "gemm_tops": ops / (t_g * 1e-3) / 1e12,
                        "gemm_frac_of_int8_peak": ops / (t_g * 1e-3) / 1e12 / INT8_PEAK_TOPS,
-                       "codes_f6_us": t_c * 1e3, "gemm_f6f6_us": t_g6 * 1e3,
+                       "codes_f6_us": t_c * 1e3, "quant_f6_us": t_q6 * 1e3, "gemm_f6f6_us": t_g6 * 1e3,
+                       "step_f6f6_us": (t_q6 + t_g6) * 1e3,
                        "gemm_f6f6_tops": ops / (t_g6 * 1e-3) / 1e12,
                        "gemm_f6f6_frac_of_int8_peak": ops / (t_g6 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
     del X, Xq, xs, Y, Wq, ws, f6w, f6x
@@ -401,9 +405,9 @@ def extra_workloads(args, dev, stream):
                           "frac_of_int8_peak": ops / (t8 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
 
     # the same chain with both GEMM operands in the FP6 operand layout: the
-    # weights packed once by spin_codes_f6 (offline, untimed); the down_proj
-    # input through spin_fwht_quant_f6, the others quantized and rewritten by
-    # spin_codes_f6 (timed)
+    # weights packed once by spin_codes_f6 (offline, untimed); every input
+    # quantized by spin_fwht_quant_f6 straight into the layout (had_n 12288
+    # for down_proj, 1 for the others), timed
     for L in layers:
         L["wf6"] = spin.spin_codes_f6(L["wq"][0])
         L["xf6"] = torch.empty((spin.f6_bytes(8192, L["K"]),), dtype=torch.uint8, device=dev)
@@ -411,11 +415,7 @@ def extra_workloads(args, dev, stream):
 
     def chain6():
         for L in layers:
-            if L["had_n"] == HAD_N:
-                spin.spin_fwht_quant_f6(L["x"], Xf6=L["xf6"], x_sum=L["xsum"], x_scale=L["sc"])
-            else:
-                xq, _, _ = spin.spin_fwht_quant(L["x"], L["had_n"], Xq=L["xq"], x_scale=L["sc"])
-                spin.spin_codes_f6(xq, L["xf6"], L["xsum"])
+            spin.spin_fwht_quant_f6(L["x"], Xf6=L["xf6"], x_sum=L["xsum"], x_scale=L["sc"], had_n=L["had_n"])
             spin.spin_w4a4_gemm_f6f6(L["xf6"], L["xsum"], L["sc"], L["wf6"][0], L["wf6"][1], L["ws"][0], L["K"],
                                      Y=L["y"])
 
@@ -423,8 +423,8 @@ def extra_workloads(args, dev, stream):
         chain6()
     t86 = _time(lambda i: chain6(), max(3, reps // 3), stream)
     out["chain_m8192_f6f6"] = {"workload": "the same chain at M=8192 with both GEMM operands in the FP6 operand "
-                                           "layout (weights packed offline; activation codes rewritten by "
-                                           "spin_codes_f6 or written by spin_fwht_quant_f6, timed)",
+                                           "layout (weights packed offline; activation codes written by "
+                                           "spin_fwht_quant_f6, timed)",
                                "us": t86 * 1e3, "tops": ops / (t86 * 1e-3) / 1e12,
                                "frac_of_int8_peak": ops / (t86 * 1e-3) / 1e12 / INT8_PEAK_TOPS}
     for L in layers:

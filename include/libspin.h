@@ -70,8 +70,9 @@ enum { SPIN_F32 = 0, SPIN_F16 = 1 };
 /* Most rows one spin_fwht_quant (and _f6, _gemm) call takes, and most
    (token, head) vectors one spin_kv_quant call takes: each kernel launch has
    fewer than 2^32 work-items in its one grid dimension, and these kernels
-   give a row 256 of them, a workgroup of 256 to 32 KV vectors. */
-#define SPIN_FWHT_MAX_M ((1 << 24) - 1)
+   give a row 256 of them (rounded up to 256 rows where rows are placed per
+   XCD), a workgroup of 256 to 32 KV vectors. */
+#define SPIN_FWHT_MAX_M ((1 << 24) - 256)
 #define SPIN_KV_MAX_VECTORS (((1LL << 24) - 1) * 32)
 /* Largest K spin_w4a4_gemm accepts: 49 * K * 256 must stay below 2^31
    (the kernel accumulates codes scaled by 16 on each side in int32). */
@@ -189,17 +190,27 @@ spin_status spin_w4a4_gemm_ex(const uint8_t* Xq, const float* x_scale, const uin
  */
 #define SPIN_F6_BYTES(M, K) ((size_t)(((M) + 31) / 32) * ((size_t)(K) / 64) * 1536)
 
+/* Longest row spin_fwht_quant_f6 quantizes without a rotation (had_n == 1). */
+#define SPIN_FWHT_F6_QUANT_MAX_K 16384
+
 /*
- * spin_fwht_quant_f6 — spin_fwht_quant (per-token INT4 after the R4 Hadamard,
- * page "SpinQuant, Reproduced", Q5) with the codes written in the FP6
- * operand layout above, for spin_w4a4_gemm_f6.
+ * spin_fwht_quant_f6 — spin_fwht_quant (per-token INT4, after the R4 Hadamard
+ * or with no rotation, page "SpinQuant, Reproduced", Q5) with the codes
+ * written in the FP6 operand layout above, for spin_w4a4_gemm_f6 and
+ * spin_w4a4_gemm_f6f6.
  *
- *   X        [M][K] float16, K == had_n == 12288
+ *   X        [M][K] float16 with K == had_n == 12288 (the down projection's
+ *            input, R4 online), or float16 / float32 with had_n == 1 (inputs
+ *            whose rotation is folded upstream: qkv_proj, o_proj, gate/up)
  *   Xf6      SPIN_F6_BYTES(M, K) bytes   OUTPUT: the codes spin_fwht_quant
- *            computes, in the FP6 operand layout
+ *            computes for the same arguments, in the FP6 operand layout
  *   x_sum    [M] int32     OUTPUT: sum_k q[m][k]
  *   x_scale  [M] float32   OUTPUT: as spin_fwht_quant
- * Requirements: x_dtype == SPIN_F16, K == had_n == 12288, M >= 0.
+ * Requirements: 0 <= M <= SPIN_FWHT_MAX_M; had_n == 12288: x_dtype ==
+ * SPIN_F16, K == 12288; had_n == 1: K % 128 == 0, SPIN_GEMM_FP6_MIN_K <= K <=
+ * SPIN_FWHT_F6_QUANT_MAX_K.
+ * Errors: SPIN_ERR_NULL, SPIN_ERR_UNSUPPORTED for another had_n or dtype,
+ * SPIN_ERR_BAD_SHAPE, SPIN_ERR_MISALIGNED (16-byte alignment).
  */
 spin_status spin_fwht_quant_f6(const void* X, spin_dtype x_dtype, int M, int K, int had_n, uint8_t* Xf6,
                                int32_t* x_sum, float* x_scale, void* stream);

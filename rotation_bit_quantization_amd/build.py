@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspin.so")
 SOURCES = ["abi.cpp", "fwht_quant.hip", "kv_quant.hip", "fold.hip", "w4a4_gemm.hip", "w4a4_gemm_fp6.hip",
-           "fwht_quant_gemm.hip", "w4a8_gemm.hip"]
+           "fwht_quant_gemm.hip", "w4a8_gemm.hip", "quant_f6.hip"]
 PROBE_LIB = os.path.join(PKG, "libspin_probe.so")
 PROBE_SOURCES = ["machine_probe.hip"]
 ARCH = "gfx950"

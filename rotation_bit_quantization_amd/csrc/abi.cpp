@@ -185,10 +185,21 @@ spin_status spin_fwht_quant_gemm_noalloc(const void* X, spin_dtype x_dtype, int 
 spin_status spin_fwht_quant_f6(const void* X, spin_dtype x_dtype, int M, int K, int had_n, uint8_t* Xf6,
                                int32_t* x_sum, float* x_scale, void* stream) {
     if (!X || !Xf6 || !x_sum || !x_scale) return SPIN_ERR_NULL;
-    if (x_dtype != SPIN_F16 || had_n != 12288) return SPIN_ERR_UNSUPPORTED;
-    if (K != 12288 || M < 0 || M > SPIN_FWHT_MAX_M) return SPIN_ERR_BAD_SHAPE;
+    if (had_n == 12288) {
+        if (x_dtype != SPIN_F16) return SPIN_ERR_UNSUPPORTED;
+        if (K != 12288) return SPIN_ERR_BAD_SHAPE;
+    } else if (had_n == 1) {
+        if (x_dtype != SPIN_F16 && x_dtype != SPIN_F32) return SPIN_ERR_UNSUPPORTED;
+        if (K % 128 != 0 || K < SPIN_GEMM_FP6_MIN_K || K > SPIN_FWHT_F6_QUANT_MAX_K) return SPIN_ERR_BAD_SHAPE;
+    } else {
+        return SPIN_ERR_UNSUPPORTED;
+    }
+    if (M < 0 || M > SPIN_FWHT_MAX_M) return SPIN_ERR_BAD_SHAPE;
     if (!aligned16(X) || !aligned16(Xf6) || !aligned16(x_sum) || !aligned16(x_scale)) return SPIN_ERR_MISALIGNED;
     if (M == 0) return SPIN_OK;
+    if (had_n == 1)
+        return from_hip(spin::launch_quant_rows_f6(X, x_dtype == SPIN_F16, M, K, Xf6, x_sum, x_scale,
+                                                   static_cast<hipStream_t>(stream)));
     return from_hip(spin::launch_fwht_quant_f6(static_cast<const __half*>(X), M, Xf6, x_sum, x_scale,
                                                static_cast<hipStream_t>(stream)));
 }

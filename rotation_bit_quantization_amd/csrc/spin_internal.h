@@ -66,6 +66,10 @@ hipError_t fwht_quant_gemm_scratch(uint32_t** out);
 // fp16 rows of 12288, H_12 (x) H_1024, INT4 codes in the FP6 operand layout + row code sums.
 hipError_t launch_fwht_quant_f6(const __half* X, int M, uint8_t* Xf6, int32_t* x_sum, float* x_scale,
                                 hipStream_t s);
+// had_n = 1: fp16 / fp32 rows of K (K % 128 == 0, K <= SPIN_FWHT_F6_QUANT_MAX_K), per-token INT4 codes in
+// the FP6 operand layout + row code sums.
+hipError_t launch_quant_rows_f6(const void* X, bool x_f16, int M, int K, uint8_t* Xf6, int32_t* x_sum,
+                                float* x_scale, hipStream_t s);
 // The FP6 GEMM on activation codes in that layout.
 hipError_t launch_w4a4_gemm_f6(const uint8_t* Xf6, const int32_t* x_sum, const float* x_scale, const uint8_t* Wq,
                                const float* w_scale, int M, int N, int K, float* Y, int32_t* acc_out,

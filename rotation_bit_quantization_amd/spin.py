@@ -215,9 +215,11 @@ def f6_bytes(M, K):
     return ((M + 31) // 32) * (K // 64) * 1536
 
 
-def spin_fwht_quant_f6(X, Xf6=None, x_sum=None, x_scale=None, stream=None):
-    """X [M, 12288] fp16 -> (Xf6 uint8 [f6_bytes(M, 12288)], x_sum [M] int32, x_scale [M] fp32)."""
-    _check(X, "X", (torch.float16,))
+def spin_fwht_quant_f6(X, Xf6=None, x_sum=None, x_scale=None, stream=None, had_n=12288):
+    """X [M, K] -> (Xf6 uint8 [f6_bytes(M, K)], x_sum [M] int32, x_scale [M] fp32).
+
+    had_n = 12288: X fp16 [M, 12288], the R4 Hadamard first; had_n = 1: X fp16 / fp32, quantized as given."""
+    _check(X, "X", (torch.float16,) if had_n == 12288 else (torch.float16, torch.float32))
     M, K = X.shape
     dev = X.device
     Xf6 = torch.empty((f6_bytes(M, K),), dtype=torch.uint8, device=dev) if Xf6 is None else Xf6
@@ -226,8 +228,8 @@ def spin_fwht_quant_f6(X, Xf6=None, x_sum=None, x_scale=None, stream=None):
     _check(Xf6, "Xf6", (torch.uint8,), (f6_bytes(M, K),))
     _check(x_sum, "x_sum", (torch.int32,), (M,))
     _check(x_scale, "x_scale", (torch.float32,), (M,))
-    st = load().spin_fwht_quant_f6(_ptr(X), SPIN_F16, M, K, K, _ptr(Xf6), _ptr(x_sum), _ptr(x_scale),
-                                   _stream(stream))
+    st = load().spin_fwht_quant_f6(_ptr(X), _dtype_code(X), M, K, int(had_n), _ptr(Xf6), _ptr(x_sum),
+                                   _ptr(x_scale), _stream(stream))
     _raise("spin_fwht_quant_f6", st)
     return Xf6, x_sum, x_scale
 

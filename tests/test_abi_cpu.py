@@ -252,6 +252,15 @@ def test_f6_pair_validation(lib):
     assert q6(M=-1) == spin.SPIN_ERR_BAD_SHAPE
     assert q6(M=1 << 24) == spin.SPIN_ERR_BAD_SHAPE
     assert q6(M=0) == spin.SPIN_OK
+    # had_n = 1 (quant only): fp16 / fp32, K % 128 == 0, 256 <= K <= SPIN_FWHT_F6_QUANT_MAX_K
+    assert q6(had=2, K=4096) == spin.SPIN_ERR_UNSUPPORTED
+    assert q6(had=1, K=4096, dt=7) == spin.SPIN_ERR_UNSUPPORTED
+    assert q6(had=1, K=4096 + 64) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(had=1, K=128) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(had=1, K=16384 + 128) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(had=1, K=4096, M=-1) == spin.SPIN_ERR_BAD_SHAPE
+    assert q6(had=1, K=4096, X=U) == spin.SPIN_ERR_MISALIGNED
+    assert q6(had=1, K=4096, dt=spin.SPIN_F32, M=0) == spin.SPIN_OK
 
     g = lib.spin_w4a4_gemm_f6
 

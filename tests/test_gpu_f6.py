@@ -60,6 +60,42 @@ def test_fwht_quant_f6_is_fwht_quant_in_the_layout(M):
     assert np.array_equal(_host(xsum), codes.astype(np.int64).sum(axis=1))
 
 
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 640), (300, 4096), (65, 12288), (33, 16384)])
+def test_quant_only_f6_is_fwht_quant_in_the_layout(M, K, dtype):
+    """had_n = 1: the codes and scales spin_fwht_quant(X, 1) writes (and the
+    oracle's, quant-only being exact), in the layout, with their row sums;
+    the both-FP6 GEMM on them gives the nibble GEMM's bits."""
+    rng = np.random.default_rng(M + K)
+    x = (rng.standard_normal((M, K)) * np.where(rng.random(K) < 0.002, 100.0, 1.0)).astype(dtype)
+    if M > 3:
+        x[3] *= dtype(1e-3)           # small row
+    if M > 5:
+        x[5] = 0                      # zero row: scale 0, codes 0
+    if M > 7:                         # values on the rounding ties of their own scale
+        x[7] = 0
+        x[7, :14] = (np.arange(14) - 6.5).astype(dtype)   # absmax 7: s = 1, y / s = k + 1/2
+        x[7, 15] = 7
+    X = _dev(x)
+    Xq, xs, _ = spin.spin_fwht_quant(X, 1)
+    Xf6, xsum, xs6 = spin.spin_fwht_quant_f6(X, had_n=1)
+    codes = oracle.unpack_int4(_host(Xq))
+    assert np.array_equal(f6_layout.decode(_host(Xf6), M, K), codes)
+    assert np.array_equal(_host(xs6).view(np.uint32), _host(xs).view(np.uint32))
+    assert np.array_equal(_host(xsum), codes.astype(np.int64).sum(axis=1))
+    pk, s_o, _ = oracle.fwht_quant(x, 1)
+    assert np.array_equal(_host(Xq), pk) and np.array_equal(_host(xs), s_o)
+    N = 96
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int64)
+    Wq = _dev(oracle.pack_int4(qw))
+    sw = _dev((rng.random(N) * 0.01).astype(np.float32))
+    Wf6, wsum = spin.spin_codes_f6(Wq)
+    Y6, acc6 = spin.spin_w4a4_gemm_f6f6(Xf6, xsum, xs6, Wf6, wsum, sw, K, want_acc=True)
+    Y, acc = spin.spin_w4a4_gemm(Xq, xs, Wq, sw, want_acc=True)
+    assert np.array_equal(_host(acc6), _host(acc))
+    assert np.array_equal(_host(Y6).view(np.uint32), _host(Y).view(np.uint32))
+
+
 def check_gemm_f6(qx, qw, sx, sw, rows=None):
     M, K = qx.shape
     Xf6 = _dev(f6_layout.encode(qx))
