@@ -61,7 +61,7 @@ def test_fwht_quant_f6_is_fwht_quant_in_the_layout(M):
 
 
 @pytest.mark.parametrize("dtype", [np.float16, np.float32])
-@pytest.mark.parametrize("M,K", [(1, 256), (37, 640), (300, 4096), (65, 12288), (33, 16384)])
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 640), (300, 4096), (65, 12288), (33, 16384), (4133, 4096)])
 def test_quant_only_f6_is_fwht_quant_in_the_layout(M, K, dtype):
     """had_n = 1: the codes and scales spin_fwht_quant(X, 1) writes (and the
     oracle's, quant-only being exact), in the layout, with their row sums;
